@@ -1,0 +1,224 @@
+"""Seeded synthetic inputs for the DSpark cross-layer context-KV write.
+
+This module only draws inputs. It holds none of the write's arithmetic (no
+projection, norm, rotation or scatter), so both the CPU oracle and the HIP
+path can take their inputs from it without sharing any of the method.
+
+Everything is returned as host numpy arrays. Activation-dtype tensors are
+returned as their 16-bit patterns (``uint16``), so the oracle and the GPU see
+identical bits.
+
+The shapes follow the draft layers the pages describe: each draft layer has a
+fused QKV projection whose rows are ``[Q | K | V]`` (sglang PR #31986,
+"_stacked_ctx_kv_params" listing: the KV slice is ``[q_size, q_size+2*kv_size)``),
+a per-head K RMSNorm weight of ``head_dim`` entries, and a neox rotary table
+``[max_position, head_dim]`` laid out as the cos half followed by the sin half
+(sglang PR #31847, "_table_qk_norm_rope_kernel" listing). The KV pool of each
+layer is ``[slots, num_kv_heads, head_dim]`` (same PR, "_build_fused_kv_write_bundle").
+
+The rotary table is an input of the write: the path only reads it. It is built
+here the way a rotary module precomputes it, with inverse frequencies
+``theta ** (-2i/D)`` and angles ``p * f_i`` evaluated in fp64 and stored as fp32.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional
+
+import numpy as np
+
+BF16 = "bf16"
+FP16 = "fp16"
+SENTINEL = 0xFFFF  # NaN in both bf16 and fp16; finite inputs never produce it
+
+
+def _to_bf16_bits(x64: np.ndarray) -> np.ndarray:
+    """fp64 -> fp32 (numpy RNE) -> bf16 bit pattern (RNE on the fp32 bits)."""
+    u = np.ascontiguousarray(x64, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def _to_fp16_bits(x64: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(x64, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def to_bits(x64: np.ndarray, dtype: str) -> np.ndarray:
+    """Convert drawn fp64 values to the activation dtype's bit patterns."""
+    if dtype == BF16:
+        return _to_bf16_bits(x64)
+    if dtype == FP16:
+        return _to_fp16_bits(x64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+@dataclasses.dataclass
+class Case:
+    """One synthetic instance of the context-KV write (host arrays)."""
+
+    name: str
+    dtype: str  # "bf16" | "fp16"
+    T: int
+    H: int
+    L: int
+    NH: int
+    D: int
+    q_size: int
+    eps: float
+    theta: float
+    P: int  # rotary table rows
+    slots: int  # pool slots per layer
+    x: np.ndarray  # uint16 [T, H]
+    qkv_w: List[np.ndarray]  # per layer uint16 [q_size + 2*kv, H]
+    qkv_b: Optional[List[np.ndarray]]  # per layer uint16 [q_size + 2*kv] or None
+    k_norm_w: List[np.ndarray]  # per layer uint16 [D]
+    table: np.ndarray  # float32 [P, D]: cos half | sin half
+    positions: np.ndarray  # int64 [T]
+    locs: np.ndarray  # int64 [T] (flattened [B, W] window when commit_lens is set)
+    commit_lens: Optional[np.ndarray]  # int64 [B] or None
+    row_width: int  # W when commit_lens is set, else 0
+
+    @property
+    def kv(self) -> int:
+        return self.NH * self.D
+
+    @property
+    def n_tot(self) -> int:
+        return self.L * 2 * self.kv
+
+    @property
+    def num_requests(self) -> int:
+        return 0 if self.commit_lens is None else len(self.commit_lens)
+
+
+def rope_table(P: int, D: int, theta: float) -> np.ndarray:
+    """Neox rotary table [P, D] fp32: row p = cos(p*f_0..f_{D/2-1}) | sin(...)."""
+    half = D // 2
+    inv_freq = theta ** (-(2.0 * np.arange(half, dtype=np.float64)) / D)
+    ang = np.arange(P, dtype=np.float64)[:, None] * inv_freq[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+def make_case(
+    *,
+    name: str = "case",
+    T: int,
+    H: int,
+    L: int,
+    NH: int,
+    D: int,
+    dtype: str = BF16,
+    bias: bool = False,
+    row_width: int = 0,
+    commit_range=(1, None),
+    theta: float = 1e4,
+    P: int = 4096,
+    slots: int = 64,
+    eps: float = 1e-6,
+    seed: int = 0,
+    q_size: Optional[int] = None,
+    locs_mode: str = "random",
+    locs_start: int = 0,
+    positions_mode: str = "uniform",
+    neg_loc_frac: float = 0.0,
+    w_std: float = 0.02,
+    x_std: float = 1.0,
+) -> Case:
+    """Draw one case. Generation order is fixed: X, per-layer Q/K/V rows, bias,
+    k_norm, positions, locs, commit_lens (then optional negative-loc holes)."""
+    if q_size is None:
+        q_size = H
+    kv = NH * D
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = to_bits(rng.standard_normal((T, H)) * x_std, dtype)
+    qkv_w = []
+    for _ in range(L):
+        q = rng.standard_normal((q_size, H))  # Q rows ~N(0,1): a wrong slice is obvious
+        k = rng.standard_normal((kv, H)) * w_std
+        v = rng.standard_normal((kv, H)) * w_std
+        qkv_w.append(to_bits(np.concatenate([q, k, v], axis=0), dtype))
+    qkv_b = None
+    if bias:
+        qkv_b = [to_bits(rng.standard_normal(q_size + 2 * kv) * 0.01, dtype) for _ in range(L)]
+    k_norm_w = [to_bits(1.0 + rng.standard_normal(D) * 0.1, dtype) for _ in range(L)]
+    if positions_mode == "uniform":
+        positions = rng.integers(0, P, size=T, dtype=np.int64)
+    elif positions_mode == "arange":
+        positions = np.arange(T, dtype=np.int64)
+    else:
+        raise ValueError(positions_mode)
+    if locs_mode == "random":
+        if T > slots:
+            raise ValueError("random injective locs need T <= slots")
+        locs = rng.permutation(slots)[:T].astype(np.int64)
+    elif locs_mode == "contiguous":
+        locs = locs_start + np.arange(T, dtype=np.int64)
+    else:
+        raise ValueError(locs_mode)
+    commit_lens = None
+    if row_width:
+        if T % row_width:
+            raise ValueError("T must be a multiple of the window width")
+        lo, hi = commit_range
+        hi = row_width if hi is None else hi
+        commit_lens = rng.integers(lo, hi + 1, size=T // row_width, dtype=np.int64)
+    if neg_loc_frac > 0:
+        holes = rng.random(T) < neg_loc_frac
+        locs = np.where(holes, -1, locs).astype(np.int64)
+    return Case(
+        name=name, dtype=dtype, T=T, H=H, L=L, NH=NH, D=D, q_size=q_size, eps=eps,
+        theta=theta, P=P, slots=slots, x=x, qkv_w=qkv_w, qkv_b=qkv_b, k_norm_w=k_norm_w,
+        table=rope_table(P, D, theta), positions=positions, locs=locs,
+        commit_lens=commit_lens, row_width=row_width,
+    )
+
+
+# The five workloads the context-KV write is measured and checked on.
+WORKLOADS = {
+    # 2 requests x 8 rows, tiny draft: 2 layers, 2 KV heads of 64.
+    "tiny": dict(T=16, H=256, L=2, NH=2, D=64, dtype=BF16, theta=1e4, P=4096, slots=64),
+    # Qwen3-8B-like decode commit: 32 requests x 8 columns, commit_lens ~ U{1..8}.
+    "decode_commit": dict(T=256, H=4096, L=5, NH=8, D=128, dtype=BF16, row_width=8,
+                          theta=1e6, P=32768, slots=65536),
+    # One 8k prompt written contiguously from slot 4096 (positions 0..8191).
+    "prefill_8k": dict(T=8192, H=4096, L=5, NH=8, D=128, dtype=BF16, theta=1e6, P=32768,
+                       slots=16384, locs_mode="contiguous", locs_start=4096,
+                       positions_mode="arange"),
+    # 16 requests x 128 rows, fp16 with a stacked per-layer KV bias.
+    "biased_fp16": dict(T=2048, H=3584, L=5, NH=4, D=128, dtype=FP16, bias=True, theta=1e6,
+                        P=32768, slots=32768),
+    # Wide hidden, head_dim 64: 64 requests x 8 columns with commit_lens.
+    "wide_gqa_d64": dict(T=512, H=7168, L=5, NH=8, D=64, dtype=BF16, row_width=8, theta=5e4,
+                         P=32768, slots=131072),
+}
+WORKLOAD_ORDER = ["tiny", "decode_commit", "prefill_8k", "biased_fp16", "wide_gqa_d64"]
+
+
+def workload(name: str) -> Case:
+    """The named workload with its fixed seed (1000 + its 1-based index)."""
+    seed = 1000 + WORKLOAD_ORDER.index(name) + 1
+    return make_case(name=name, seed=seed, **WORKLOADS[name])
+
+
+def hand_case(pos: int) -> Case:
+    """The hand-worked case: T=1, H=4, L=1, NH=1, D=4, Q rows 99, W_K=I, W_V=2I,
+    no bias, k_norm weight 1, eps 0, theta 1e4, X = [1, 2, 3, 4]."""
+    H = D = 4
+    w = np.concatenate([np.full((4, 4), 99.0), np.eye(4), 2.0 * np.eye(4)], axis=0)
+    return Case(
+        name=f"hand_pos{pos}", dtype=BF16, T=1, H=H, L=1, NH=1, D=D, q_size=4, eps=0.0,
+        theta=1e4, P=16, slots=4,
+        x=to_bits(np.array([[1.0, 2.0, 3.0, 4.0]]), BF16),
+        qkv_w=[to_bits(w, BF16)], qkv_b=None, k_norm_w=[to_bits(np.ones(4), BF16)],
+        table=rope_table(16, D, 1e4), positions=np.array([pos], dtype=np.int64),
+        locs=np.array([2], dtype=np.int64), commit_lens=None, row_width=0,
+    )
+
+
+def sentinel_pools(case: Case) -> tuple:
+    """Per-layer K and V pools [slots, NH, D] filled with the 0xFFFF sentinel."""
+    shape = (case.slots, case.NH, case.D)
+    ks = [np.full(shape, SENTINEL, dtype=np.uint16) for _ in range(case.L)]
+    vs = [np.full(shape, SENTINEL, dtype=np.uint16) for _ in range(case.L)]
+    return ks, vs
