@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused context-KV write on one MI355X.
+
+One step = one dspark_ctx_kv_write over one batch of the workload (GEMM + K
+RMSNorm + neox RoPE + scatter into every layer's pool), inputs resident in HBM.
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+Timing: W warmup steps, then exactly K steps, each bracketed by a device
+synchronisation. The steps are captured into a HIP graph first, so host launch
+overhead (a ctypes call per step) does not pace the device; every step still
+runs the full write. Successive steps use different packed copies of the
+stacked weight, enough copies to exceed the 256 MB Infinity Cache, so each
+step streams its weights from HBM as it would after a target-model forward.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "context-KV rows/s (fused GEMM+norm+RoPE+write); % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
+INFINITY_CACHE_BYTES = 256 << 20
+KERNEL_SOURCE = os.path.join(ROOT, "speculative_decoding_draft_stacked_amd", "csrc",
+                             "ctx_kv_write.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(case, written_rows: int) -> dict:
+    """Algorithmic FLOPs and HBM bytes of one write: every row is projected;
+    bytes = stacked weight + hidden + bias + fp32 k_norm + one table row per
+    token + index arrays + the written pool rows."""
+    s = 2
+    n_tot = case.n_tot
+    flops = 2.0 * case.T * n_tot * case.H
+    nbytes = (n_tot * case.H * s + case.T * case.H * s
+              + (n_tot * s if case.qkv_b is not None else 0)
+              + case.L * case.D * 4 + case.T * case.D * 4 + 16 * case.T
+              + 8 * case.num_requests + written_rows * n_tot * s)
+    return {"flops": flops, "bytes": float(nbytes)}
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_sha") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(case, seconds: float) -> dict:
+    """The CPU oracle on the same batch, repeated for about `seconds`."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import ctx_kv_oracle as O
+    from speculative_decoding_draft_stacked_amd import workloads as W
+
+    ks, vs = W.sentinel_pools(case)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        O.ctx_kv_write(case, ks, vs)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    del ks, vs, np
+    return {"value": case.T * reps / el, "unit": "rows/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{reps} full passes of the {case.name} batch ({case.T} rows, {case.L} "
+                      f"layers) in {el:.1f} s; numpy fp64, BLAS threads = {threads}"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_commit")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch steps one by one (no graph)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} (WORLD_SIZE={world}) is not "
+              "supported: the context-KV write is benchmarked on a single MI355X.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import speculative_decoding_draft_stacked_amd as dk
+    from speculative_decoding_draft_stacked_amd import workloads as W
+    from speculative_decoding_draft_stacked_amd.harness import DeviceCase
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    dk.lib()
+    torch.cuda.set_device(0)
+
+    log(f"[bench] generating workload {args.workload}")
+    case = W.workload(args.workload)
+    valid = (case.locs >= 0)
+    if case.commit_lens is not None:
+        t = np.arange(case.T)
+        valid &= (t % case.row_width) < case.commit_lens[t // case.row_width]
+    written = int(valid.sum())
+    alg = algorithmic(case, written)
+
+    dc = DeviceCase(case)
+    w_bytes = case.n_tot * case.H * 2
+    copies = max(1, math.ceil(2 * INFINITY_CACHE_BYTES / w_bytes))
+    packs = [dc.pack() for _ in range(copies)]
+    pools = dc.pool_descs()
+    commit = dc.commit
+    W_ = case.row_width if commit is not None else None
+    log(f"[bench] T={case.T} H={case.H} L={case.L} NH={case.NH} D={case.D} {case.dtype}, "
+        f"written rows {written}, weight copies {copies}")
+
+    def step(i):
+        ok = dk.ctx_kv_write(packs[i % copies], dc.x, dc.positions, dc.locs, pools,
+                             commit_lens=commit, locs_row_width=W_)
+        if not ok:
+            raise RuntimeError("write fell back")
+
+    # warmup (eager) also validates the launch path before capture
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    if args.eager:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        for i in range(args.steps):
+            step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        gpu_ms = e0.elapsed_time(e1)
+        launch = "eager"
+    else:
+        side = torch.cuda.Stream()
+        g_warm, g_main = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g_warm, stream=side):
+                for i in range(args.warmup):
+                    step(i)
+            with torch.cuda.graph(g_main, stream=side):
+                for i in range(args.steps):
+                    step(i)
+        g_warm.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        g_main.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        gpu_ms = e0.elapsed_time(e1)
+        launch = "hip_graph"
+    assert packs[0].range_errors() == 0
+    log(f"[bench] {args.steps} steps: device {gpu_ms:.3f} ms, wall {wall * 1e3:.3f} ms")
+
+    ms_per_step = gpu_ms / args.steps
+    t_kernel = ms_per_step * 1e-3  # one kernel per step
+    ridge = MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if alg["flops"] / alg["bytes"] < ridge:
+        ach = alg["bytes"] / t_kernel / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    else:
+        ach = alg["flops"] / t_kernel / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_PEAK_TFLOPS, 4)}
+    roof["traffic"] = measured_traffic(args.workload)
+
+    out = {
+        "metric": METRIC,
+        "value": round(case.T / t_kernel, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.dtype,
+        "data": "synthetic: seeded random inputs and random-init weights of the workload's shape",
+        "config": {"workload": args.workload, "T": case.T, "H": case.H, "L": case.L,
+                   "kv_heads": case.NH, "head_dim": case.D, "written_rows": written,
+                   "weight_copies": copies, "launch": launch,
+                   "algorithmic_bytes": alg["bytes"], "flops": alg["flops"]},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the CPU oracle for ~{args.cpu_seconds} s")
+        out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    for p in packs:
+        p.free()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

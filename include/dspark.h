@@ -1,0 +1,196 @@
+/*
+ * dspark.h - C ABI of the DSpark cross-layer context-KV write for MI355X (gfx950).
+ *
+ * The operation (sglang PR #31986 "stack every DSpark layer's KV projection into
+ * one GEMM", key source snippets; sglang PR #31847 "[spec decoding] support
+ * inkling dspark", key source snippets): every draft layer's K/V rows of its
+ * fused QKV projection are stacked into one weight W_stacked [L*2*kv, H]. The
+ * shared ctx_hidden [T, H] goes through one GEMM against it (plus the stacked
+ * bias when every layer has one). Per layer and per KV head, K then gets an
+ * fp32 RMSNorm with that layer's k_norm weight and the shared eps, and a neox
+ * rotation read from a cos/sin table at the row's position. K and the raw V are
+ * scattered into each layer's KV pool at the row's slot.
+ *
+ * Numerics: fp32 accumulation; the GEMM output is rounded to the activation
+ * dtype, the normalised K is rounded again, and the rotated K once more
+ * (round-to-nearest-even each time), as in the per-layer eager path.
+ *
+ * Conventions for every call:
+ *   - "device" pointers are HIP device memory of the device that is current on
+ *     the calling thread; "host" pointers are ordinary host memory.
+ *   - Element strides are in elements, not bytes.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.
+ *   - Status codes are the DSPARK_* values below. A call that returns anything
+ *     but DSPARK_OK has enqueued no device work.
+ *   - The library never synchronises the stream in dspark_ctx_kv_write and
+ *     allocates nothing there, so the call can be captured in a HIP graph.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ status */
+enum {
+  DSPARK_OK = 0,
+  DSPARK_FALLBACK = 1,     /* not eligible: the caller runs its per-layer path */
+  DSPARK_E_INVALID = -1,   /* misuse: bad pointer, size or argument pairing */
+  DSPARK_E_DEVICE = -3,    /* a HIP runtime call failed */
+  DSPARK_E_NOMEM = -4      /* device allocation failed (pack only) */
+};
+
+/* Why a pack or a write returned DSPARK_FALLBACK. */
+enum {
+  DSPARK_FB_NONE = 0,
+  DSPARK_FB_NO_LAYERS = 1,       /* zero layers */
+  DSPARK_FB_TOO_MANY_LAYERS = 2, /* more than DSPARK_MAX_LAYERS */
+  DSPARK_FB_NOT_SLICEABLE = 3,   /* weight quantized, of another dtype, or not row-sliceable */
+  DSPARK_FB_EPS_MISMATCH = 4,    /* layers disagree on the k_norm epsilon */
+  DSPARK_FB_MIXED_BIAS = 5,      /* some layers have a QKV bias and some do not */
+  DSPARK_FB_SHAPE = 6,           /* head_dim / kv_size differ across layers or are unsupported */
+  DSPARK_FB_DTYPE = 7,           /* activation or k_norm dtype unsupported */
+  DSPARK_FB_KV_SCALE = 8,        /* a K/V quantization scale is attached */
+  DSPARK_FB_ROPE = 9,            /* rotary is not neox full-dim over one shared fp32 table */
+  DSPARK_FB_POOL_LAYOUT = 10     /* pool dtype, head layout or alignment unsupported */
+};
+
+/* Element types. */
+enum { DSPARK_BF16 = 0, DSPARK_FP16 = 1, DSPARK_FP32 = 2, DSPARK_QUANTIZED = 99 };
+
+#define DSPARK_MAX_LAYERS 32
+
+/* One draft layer's attention parameters, as the layer holds them.
+ * qkv_weight: device, w_rows x hidden, element (r, c) at r*w_row_stride +
+ *   c*w_col_stride; rows are [Q: q_size | K: kv_size | V: kv_size | ...].
+ *   The K/V slice is rows [q_size, q_size + 2*kv_size) (sglang PR #31986,
+ *   "_stacked_ctx_kv_params"). Sliceable means w_dtype equals the activation
+ *   dtype, w_col_stride == 1 and w_rows >= q_size + 2*kv_size.
+ * qkv_bias: device [w_rows] contiguous, same dtype, or NULL.
+ * k_norm_weight: device [head_dim] contiguous, dtype bf16, fp16 or fp32.
+ * rope_cos_sin: device [rope_max_pos, rope_dim] fp32, row p = cos half | sin half.
+ */
+typedef struct {
+  const void* qkv_weight;
+  int64_t w_rows;
+  int64_t w_row_stride;
+  int64_t w_col_stride;
+  int32_t w_dtype;
+  const void* qkv_bias;
+  const void* k_norm_weight;
+  int32_t k_norm_dtype;
+  double k_norm_eps;
+  int64_t q_size;
+  int64_t kv_size;
+  int64_t head_dim;
+  int32_t has_kv_scale;
+  const void* rope_cos_sin;
+  int32_t rope_dtype;
+  int64_t rope_max_pos;
+  int64_t rope_dim;
+  int32_t rope_is_neox;
+} dspark_layer_desc;
+
+/* One layer's KV pool: device buffers [num_slots, num_kv_heads, head_dim].
+ * Supported layout (else DSPARK_FALLBACK / DSPARK_FB_POOL_LAYOUT, as the
+ * reference's bundle builder requires in sglang PR #31847): dtype equal to the
+ * activation dtype, stride1 == head_dim, stride2 == 1, stride0 >= num_kv_heads *
+ * head_dim, base pointers 16-byte aligned and stride0 a multiple of 8. */
+typedef struct {
+  void* k;
+  void* v;
+  int64_t num_slots;
+  int64_t k_stride0, k_stride1, k_stride2;
+  int64_t v_stride0, v_stride1, v_stride2;
+  int32_t dtype;
+} dspark_pool_desc;
+
+typedef struct dspark_ctx_kv_pack dspark_ctx_kv_pack; /* opaque */
+
+/* Eligibility of a set of layers for the stacked write, host-only: reads the
+ * descriptors, never dereferences a device pointer. Checks (sglang PR #31986
+ * "_stacked_ctx_kv_params" and PR #31847 "_build_fused_kv_write_bundle"):
+ * at least one and at most DSPARK_MAX_LAYERS layers; every weight sliceable;
+ * equal k_norm eps; bias present in all layers or none; equal head_dim and
+ * kv_size with kv_size % head_dim == 0, head_dim in {64, 128}, hidden % 8 == 0;
+ * act_dtype bf16 or fp16; no K/V scale; neox rotary with rope_dim == head_dim
+ * over an fp32 table of the same shape in every layer.
+ * Returns DSPARK_OK, or DSPARK_FALLBACK with *fallback_reason set (may be NULL),
+ * or DSPARK_E_INVALID for a NULL `layers` with num_layers > 0 or hidden <= 0.
+ * When two layers' table pointers differ, only dspark_pack_ctx_kv can compare
+ * their contents; this call then assumes they are equal. */
+int dspark_check_eligibility(const dspark_layer_desc* layers, int32_t num_layers,
+                             int64_t hidden, int32_t act_dtype, int32_t* fallback_reason);
+
+/* Builds the stacked parameters once (sglang PR #31986: cached stack of weight,
+ * bias and fp32 k_norm weights). Runs dspark_check_eligibility, compares rotary
+ * tables whose pointers differ, then allocates and fills on `stream`:
+ * W_stacked [L*2*kv, hidden] (layer-major, K rows then V rows), the stacked bias
+ * [L*2*kv] when present, k_norm [L, head_dim] widened to fp32. The rotary table
+ * of layer 0 is referenced, not copied: it must outlive the pack. Synchronises
+ * `stream` before returning, so the source weights may change afterwards; the
+ * pack then still holds the old values (re-pack after a weight update).
+ * Returns DSPARK_OK with *out set, DSPARK_FALLBACK with *fallback_reason set
+ * (*out = NULL), DSPARK_E_INVALID (NULL out), DSPARK_E_NOMEM or DSPARK_E_DEVICE. */
+int dspark_pack_ctx_kv(const dspark_layer_desc* layers, int32_t num_layers, int64_t hidden,
+                       int32_t act_dtype, void* stream, dspark_ctx_kv_pack** out,
+                       int32_t* fallback_reason);
+
+/* The write: one GEMM of ctx_hidden against W_stacked, then per layer and K head
+ * RMSNorm + neox rotation, and the scatter of K and raw V into the pools.
+ *   ctx_hidden: device [num_tokens, hidden] in the activation dtype, row stride
+ *     hidden_row_stride (>= hidden, multiple of 8), 16-byte aligned.
+ *   positions: device int64 [num_tokens], each in [0, rope_max_pos).
+ *   locs: device int64 [num_tokens]; a row with loc < 0 is not written
+ *     (sglang PR #31847, "fused_kv_norm_rope_write").
+ *   commit_lens: device int64 [num_requests] or NULL. When given, locs is a
+ *     flattened [num_requests, locs_row_width] window and only columns
+ *     c < commit_lens[b] of request b are written; other slots stay untouched.
+ *     commit_lens and locs_row_width > 0 must come together, and
+ *     num_requests * locs_row_width == num_tokens (else DSPARK_E_INVALID).
+ *     Without commit_lens, locs_row_width and num_requests must be 0.
+ *   pools: host array of num_pools == L descriptors, layer order of the pack.
+ * Valid slots must be distinct (the scatter is not ordered between rows).
+ * A row whose position is outside [0, rope_max_pos) or whose loc is
+ * >= that layer's num_slots is not written and is counted in the pack's range
+ * error counter (dspark_pack_range_errors); no memory outside the given
+ * buffers is ever accessed.
+ * num_tokens == 0 returns DSPARK_OK with nothing enqueued.
+ * Returns DSPARK_OK (enqueued on `stream`), DSPARK_FALLBACK with
+ * *fallback_reason (may be NULL) = DSPARK_FB_POOL_LAYOUT, DSPARK_E_INVALID,
+ * or DSPARK_E_DEVICE. */
+int dspark_ctx_kv_write(const dspark_ctx_kv_pack* pack, const void* ctx_hidden,
+                        int64_t num_tokens, int64_t hidden_row_stride,
+                        const int64_t* positions, const int64_t* locs,
+                        const int64_t* commit_lens, int64_t locs_row_width,
+                        int64_t num_requests, const dspark_pool_desc* pools,
+                        int32_t num_pools, void* stream, int32_t* fallback_reason);
+
+/* Reads and clears the pack's count of rows skipped for an out-of-range
+ * position or slot. Synchronises `stream`. Returns DSPARK_OK or an error. */
+int dspark_pack_range_errors(const dspark_ctx_kv_pack* pack, void* stream, int64_t* count);
+
+/* Shape of a pack (host-only). Any output pointer may be NULL. */
+int dspark_pack_info(const dspark_ctx_kv_pack* pack, int32_t* num_layers, int64_t* hidden,
+                     int64_t* kv_size, int64_t* head_dim, int32_t* act_dtype,
+                     int32_t* has_bias);
+
+/* Device pointers of the pack's stacked weight [L*2*kv, hidden], bias (NULL if
+ * none) and fp32 k_norm [L, head_dim], for inspection. Owned by the pack. */
+int dspark_pack_buffers(const dspark_ctx_kv_pack* pack, const void** w_stacked,
+                        const void** bias, const float** k_norm);
+
+/* Frees the pack's device buffers (waits for the device first). NULL is a no-op. */
+void dspark_pack_free(dspark_ctx_kv_pack* pack);
+
+/* Static strings for a status code and a fallback reason. */
+const char* dspark_status_str(int status);
+const char* dspark_fallback_str(int reason);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSPARK_H */

@@ -1,0 +1,281 @@
+"""Python binding of libdspark (the DSpark cross-layer context-KV write on MI355X).
+
+Argument marshalling only: every step of the write runs in the HIP library.
+Torch tensors are accepted for convenience; only their device pointers,
+strides, dtypes and the current stream are read here. If the library is not
+built, every call raises.
+
+Entry points mirror the C ABI in include/dspark.h:
+  check_eligibility(layers, hidden, act_dtype)      -> (status, reason)
+  pack_ctx_kv(layers, hidden, act_dtype, stream)    -> Pack | None (None = fallback)
+  ctx_kv_write(pack, ctx_hidden, positions, locs, pools, commit_lens=None,
+               locs_row_width=None, stream=None)    -> True (enqueued) | False (fallback)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdspark.so")
+
+OK, FALLBACK, E_INVALID, E_DEVICE, E_NOMEM = 0, 1, -1, -3, -4
+BF16, FP16, FP32, QUANTIZED = 0, 1, 2, 99
+MAX_LAYERS = 32
+FALLBACK_REASONS = {
+    0: "NONE", 1: "NO_LAYERS", 2: "TOO_MANY_LAYERS", 3: "NOT_SLICEABLE", 4: "EPS_MISMATCH",
+    5: "MIXED_BIAS", 6: "SHAPE", 7: "DTYPE", 8: "KV_SCALE", 9: "ROPE", 10: "POOL_LAYOUT",
+}
+EXPORTS = [
+    "dspark_check_eligibility", "dspark_pack_ctx_kv", "dspark_ctx_kv_write",
+    "dspark_pack_range_errors", "dspark_pack_info", "dspark_pack_buffers", "dspark_pack_free",
+    "dspark_status_str", "dspark_fallback_str",
+]
+
+
+class LayerDesc(ctypes.Structure):
+    """Mirror of dspark_layer_desc."""
+
+    _fields_ = [
+        ("qkv_weight", ctypes.c_void_p),
+        ("w_rows", ctypes.c_int64),
+        ("w_row_stride", ctypes.c_int64),
+        ("w_col_stride", ctypes.c_int64),
+        ("w_dtype", ctypes.c_int32),
+        ("qkv_bias", ctypes.c_void_p),
+        ("k_norm_weight", ctypes.c_void_p),
+        ("k_norm_dtype", ctypes.c_int32),
+        ("k_norm_eps", ctypes.c_double),
+        ("q_size", ctypes.c_int64),
+        ("kv_size", ctypes.c_int64),
+        ("head_dim", ctypes.c_int64),
+        ("has_kv_scale", ctypes.c_int32),
+        ("rope_cos_sin", ctypes.c_void_p),
+        ("rope_dtype", ctypes.c_int32),
+        ("rope_max_pos", ctypes.c_int64),
+        ("rope_dim", ctypes.c_int64),
+        ("rope_is_neox", ctypes.c_int32),
+    ]
+
+
+class PoolDesc(ctypes.Structure):
+    """Mirror of dspark_pool_desc."""
+
+    _fields_ = [
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("num_slots", ctypes.c_int64),
+        ("k_stride0", ctypes.c_int64),
+        ("k_stride1", ctypes.c_int64),
+        ("k_stride2", ctypes.c_int64),
+        ("v_stride0", ctypes.c_int64),
+        ("v_stride1", ctypes.c_int64),
+        ("v_stride2", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m speculative_decoding_draft_stacked_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        p_i32, p_i64 = ctypes.POINTER(i32), ctypes.POINTER(i64)
+        L.dspark_check_eligibility.argtypes = [ctypes.POINTER(LayerDesc), i32, i64, i32, p_i32]
+        L.dspark_pack_ctx_kv.argtypes = [ctypes.POINTER(LayerDesc), i32, i64, i32, vp,
+                                         ctypes.POINTER(vp), p_i32]
+        L.dspark_ctx_kv_write.argtypes = [vp, vp, i64, i64, vp, vp, vp, i64, i64,
+                                          ctypes.POINTER(PoolDesc), i32, vp, p_i32]
+        L.dspark_pack_range_errors.argtypes = [vp, vp, p_i64]
+        L.dspark_pack_info.argtypes = [vp, p_i32, p_i64, p_i64, p_i64, p_i32, p_i32]
+        L.dspark_pack_buffers.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                          ctypes.POINTER(vp)]
+        L.dspark_pack_free.argtypes = [vp]
+        L.dspark_pack_free.restype = None
+        L.dspark_status_str.argtypes = [ctypes.c_int]
+        L.dspark_status_str.restype = ctypes.c_char_p
+        L.dspark_fallback_str.argtypes = [ctypes.c_int]
+        L.dspark_fallback_str.restype = ctypes.c_char_p
+        for name in ("dspark_check_eligibility", "dspark_pack_ctx_kv", "dspark_ctx_kv_write",
+                     "dspark_pack_range_errors", "dspark_pack_info", "dspark_pack_buffers"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().dspark_status_str(status).decode()
+
+
+def fallback_str(reason: int) -> str:
+    return lib().dspark_fallback_str(reason).decode()
+
+
+def _raise_for(status: int, what: str):
+    if status == E_INVALID:
+        raise ValueError(f"{what}: {status_str(status)}")
+    if status < 0:
+        raise RuntimeError(f"{what}: {status_str(status)} ({status})")
+
+
+def _layers_array(layers: Sequence[LayerDesc]):
+    arr = (LayerDesc * max(len(layers), 1))(*layers)
+    return arr
+
+
+def check_eligibility(layers: Sequence[LayerDesc], hidden: int, act_dtype: int):
+    """(status, reason) of dspark_check_eligibility; host-only."""
+    reason = ctypes.c_int32(-1)
+    st = lib().dspark_check_eligibility(_layers_array(layers), len(layers), hidden, act_dtype,
+                                        ctypes.byref(reason))
+    return st, reason.value
+
+
+class Pack:
+    """Owner of a dspark_ctx_kv_pack handle."""
+
+    def __init__(self, handle: int):
+        self.handle = handle
+
+    @property
+    def as_parameter(self):
+        if not self.handle:
+            raise ValueError("pack already freed")
+        return ctypes.c_void_p(self.handle)
+
+    def info(self) -> dict:
+        L, H, kv, D, dt, b = (ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64(),
+                              ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32())
+        _raise_for(lib().dspark_pack_info(self.as_parameter, ctypes.byref(L), ctypes.byref(H),
+                                          ctypes.byref(kv), ctypes.byref(D), ctypes.byref(dt),
+                                          ctypes.byref(b)), "dspark_pack_info")
+        return dict(num_layers=L.value, hidden=H.value, kv_size=kv.value, head_dim=D.value,
+                    act_dtype=dt.value, has_bias=bool(b.value))
+
+    def buffers(self):
+        w, b, k = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_void_p()
+        _raise_for(lib().dspark_pack_buffers(self.as_parameter, ctypes.byref(w), ctypes.byref(b),
+                                             ctypes.byref(k)), "dspark_pack_buffers")
+        return w.value, b.value, k.value
+
+    def range_errors(self, stream=None) -> int:
+        n = ctypes.c_int64()
+        _raise_for(lib().dspark_pack_range_errors(self.as_parameter, _stream(stream),
+                                                  ctypes.byref(n)), "dspark_pack_range_errors")
+        return n.value
+
+    def free(self):
+        if self.handle:
+            lib().dspark_pack_free(ctypes.c_void_p(self.handle))
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def _stream(stream) -> Optional[int]:
+    """A hipStream_t as an integer: torch streams, raw integers or None (current torch stream)."""
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def pack_ctx_kv(layers: Sequence[LayerDesc], hidden: int, act_dtype: int, stream=None):
+    """Pack the stacked parameters. Returns a Pack, or None when the layers are
+    not eligible (the caller then runs its per-layer path); `last_fallback_reason`
+    holds the reason."""
+    global last_fallback_reason
+    h = ctypes.c_void_p()
+    reason = ctypes.c_int32(0)
+    st = lib().dspark_pack_ctx_kv(_layers_array(layers), len(layers), hidden, act_dtype,
+                                  _stream(stream), ctypes.byref(h), ctypes.byref(reason))
+    last_fallback_reason = reason.value
+    if st == FALLBACK:
+        return None
+    _raise_for(st, "dspark_pack_ctx_kv")
+    return Pack(h.value)
+
+
+last_fallback_reason = 0
+
+
+def ctx_kv_write_raw(pack: Pack, ctx_hidden: int, num_tokens: int, hidden_row_stride: int,
+                     positions: int, locs: int, commit_lens: Optional[int], locs_row_width: int,
+                     num_requests: int, pools: Sequence[PoolDesc], stream) -> int:
+    """dspark_ctx_kv_write on raw device pointers; returns (status, reason)."""
+    arr = (PoolDesc * max(len(pools), 1))(*pools)
+    reason = ctypes.c_int32(0)
+    st = lib().dspark_ctx_kv_write(pack.as_parameter, ctx_hidden, num_tokens, hidden_row_stride,
+                                   positions, locs, commit_lens, locs_row_width, num_requests,
+                                   arr, len(pools), _stream(stream), ctypes.byref(reason))
+    return st, reason.value
+
+
+# ------------------------------------------------------------------ torch plumbing
+
+def _dtype_code(t) -> int:
+    import torch
+    return {torch.bfloat16: BF16, torch.float16: FP16, torch.float32: FP32}.get(t.dtype, QUANTIZED)
+
+
+def layer_desc(qkv_weight, k_norm_weight, eps: float, q_size: int, kv_size: int, head_dim: int,
+               cos_sin_cache, qkv_bias=None, has_kv_scale: bool = False,
+               is_neox: bool = True, rotary_dim: Optional[int] = None) -> LayerDesc:
+    """Descriptor of one layer from its tensors (pointers and strides only)."""
+    return LayerDesc(
+        qkv_weight=qkv_weight.data_ptr(), w_rows=qkv_weight.shape[0],
+        w_row_stride=qkv_weight.stride(0), w_col_stride=qkv_weight.stride(1),
+        w_dtype=_dtype_code(qkv_weight),
+        qkv_bias=None if qkv_bias is None else qkv_bias.data_ptr(),
+        k_norm_weight=k_norm_weight.data_ptr(), k_norm_dtype=_dtype_code(k_norm_weight),
+        k_norm_eps=eps, q_size=q_size, kv_size=kv_size, head_dim=head_dim,
+        has_kv_scale=int(has_kv_scale), rope_cos_sin=cos_sin_cache.data_ptr(),
+        rope_dtype=_dtype_code(cos_sin_cache), rope_max_pos=cos_sin_cache.shape[0],
+        rope_dim=cos_sin_cache.shape[1] if rotary_dim is None else rotary_dim,
+        rope_is_neox=int(is_neox),
+    )
+
+
+def pool_desc(k_buf, v_buf) -> PoolDesc:
+    """Descriptor of one layer's pool from its [slots, NH, D] K and V buffers."""
+    return PoolDesc(k=k_buf.data_ptr(), v=v_buf.data_ptr(), num_slots=k_buf.shape[0],
+                    k_stride0=k_buf.stride(0), k_stride1=k_buf.stride(1),
+                    k_stride2=k_buf.stride(2), v_stride0=v_buf.stride(0),
+                    v_stride1=v_buf.stride(1), v_stride2=v_buf.stride(2),
+                    dtype=_dtype_code(k_buf) if _dtype_code(k_buf) == _dtype_code(v_buf)
+                    else QUANTIZED)
+
+
+def ctx_kv_write(pack: Pack, ctx_hidden, positions, locs, pools: Sequence[PoolDesc],
+                 commit_lens=None, locs_row_width: Optional[int] = None, stream=None) -> bool:
+    """Enqueue the write. True when enqueued, False on fallback (nothing
+    written). ValueError on misuse (e.g. commit_lens without locs_row_width)."""
+    if (commit_lens is None) != (locs_row_width is None):
+        raise ValueError("commit_lens and locs_row_width must be passed together")
+    T = ctx_hidden.shape[0]
+    W = 0 if commit_lens is None else int(locs_row_width)
+    B = 0 if commit_lens is None else commit_lens.numel()
+    st, reason = ctx_kv_write_raw(
+        pack, ctx_hidden.data_ptr(), T, ctx_hidden.stride(0), positions.data_ptr(),
+        locs.data_ptr(), None if commit_lens is None else commit_lens.data_ptr(), W, B, pools,
+        stream)
+    if st == FALLBACK:
+        return False
+    _raise_for(st, "dspark_ctx_kv_write")
+    return True

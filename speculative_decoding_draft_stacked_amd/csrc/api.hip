@@ -1,0 +1,309 @@
+// C ABI of the context-KV write library: eligibility, pack, write, strings.
+//
+// Eligibility follows the fast-path-or-fallback pattern of sglang PR #31986
+// ("_stacked_ctx_kv_params": sliceable weights, equal eps, consistent bias) and
+// sglang PR #31847 ("_build_fused_kv_write_bundle": no K/V scale, equal head
+// shape, neox full-dim rotary over one shared table, pool dtype and head-major
+// layout). Every reason is reported instead of falling back silently.
+#include <new>
+
+#include "internal.h"
+
+struct dspark_ctx_kv_pack {
+  int device;
+  int32_t num_layers;
+  int64_t hidden;
+  int64_t kv_size;
+  int64_t head_dim;
+  int32_t dtype;
+  int32_t has_bias;
+  float eps;
+  uint16_t* w;               // [L * 2 * kv, hidden]
+  uint16_t* bias;            // [L * 2 * kv] or nullptr
+  float* knw;                // [L, head_dim]
+  const float* table;        // [P, head_dim], caller-owned
+  int64_t table_rows;
+  unsigned long long* err;   // range error counter
+};
+
+namespace {
+
+void set_reason(int32_t* out, int32_t r) {
+  if (out) *out = r;
+}
+
+int fallback(int32_t* out, int32_t r) {
+  set_reason(out, r);
+  return DSPARK_FALLBACK;
+}
+
+bool is_act_dtype(int32_t d) { return d == DSPARK_BF16 || d == DSPARK_FP16; }
+
+void free_pack(dspark_ctx_kv_pack* p) {
+  if (!p) return;
+  if (p->w) (void)hipFree(p->w);
+  if (p->bias) (void)hipFree(p->bias);
+  if (p->knw) (void)hipFree(p->knw);
+  if (p->err) (void)hipFree(p->err);
+  delete p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dspark_check_eligibility(const dspark_layer_desc* layers, int32_t num_layers, int64_t hidden,
+                             int32_t act_dtype, int32_t* fallback_reason) {
+  set_reason(fallback_reason, DSPARK_FB_NONE);
+  if (num_layers < 0 || hidden <= 0 || (num_layers > 0 && !layers)) return DSPARK_E_INVALID;
+  if (num_layers == 0) return fallback(fallback_reason, DSPARK_FB_NO_LAYERS);
+  if (num_layers > DSPARK_MAX_LAYERS) return fallback(fallback_reason, DSPARK_FB_TOO_MANY_LAYERS);
+  if (!is_act_dtype(act_dtype)) return fallback(fallback_reason, DSPARK_FB_DTYPE);
+  const dspark_layer_desc& l0 = layers[0];
+  for (int32_t i = 0; i < num_layers; ++i) {
+    const dspark_layer_desc& d = layers[i];
+    if (!d.qkv_weight || !d.k_norm_weight) return DSPARK_E_INVALID;
+    const bool sliceable = d.w_dtype == act_dtype && d.w_col_stride == 1 && d.q_size >= 0 &&
+                           d.kv_size > 0 && d.w_rows >= d.q_size + 2 * d.kv_size &&
+                           d.w_row_stride >= hidden;
+    if (!sliceable) return fallback(fallback_reason, DSPARK_FB_NOT_SLICEABLE);
+    if (d.k_norm_eps != l0.k_norm_eps) return fallback(fallback_reason, DSPARK_FB_EPS_MISMATCH);
+    if (d.has_kv_scale) return fallback(fallback_reason, DSPARK_FB_KV_SCALE);
+    if (d.head_dim != l0.head_dim || d.kv_size != l0.kv_size)
+      return fallback(fallback_reason, DSPARK_FB_SHAPE);
+    if (!d.rope_is_neox || d.rope_dim != d.head_dim || d.rope_dtype != DSPARK_FP32 ||
+        !d.rope_cos_sin || d.rope_max_pos <= 0 || d.rope_max_pos != l0.rope_max_pos)
+      return fallback(fallback_reason, DSPARK_FB_ROPE);
+    if (d.k_norm_dtype != DSPARK_BF16 && d.k_norm_dtype != DSPARK_FP16 &&
+        d.k_norm_dtype != DSPARK_FP32)
+      return fallback(fallback_reason, DSPARK_FB_DTYPE);
+  }
+  for (int32_t i = 0; i < num_layers; ++i)
+    if ((layers[i].qkv_bias != nullptr) != (l0.qkv_bias != nullptr))
+      return fallback(fallback_reason, DSPARK_FB_MIXED_BIAS);
+  const int64_t D = l0.head_dim;
+  if ((D != 64 && D != 128) || l0.kv_size % D != 0 || hidden % 8 != 0 ||
+      l0.w_row_stride % 8 != 0)
+    return fallback(fallback_reason, DSPARK_FB_SHAPE);
+  return DSPARK_OK;
+}
+
+int dspark_pack_ctx_kv(const dspark_layer_desc* layers, int32_t num_layers, int64_t hidden,
+                       int32_t act_dtype, void* stream_ptr, dspark_ctx_kv_pack** out,
+                       int32_t* fallback_reason) {
+  if (!out) return DSPARK_E_INVALID;
+  *out = nullptr;
+  const int st = dspark_check_eligibility(layers, num_layers, hidden, act_dtype, fallback_reason);
+  if (st != DSPARK_OK) return st;
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  for (int32_t i = 0; i < num_layers; ++i) {
+    // 16-byte vector reads of every weight row need an aligned base
+    if (reinterpret_cast<uintptr_t>(layers[i].qkv_weight) % 16 != 0)
+      return fallback(fallback_reason, DSPARK_FB_NOT_SLICEABLE);
+  }
+
+  dspark_ctx_kv_pack* p = new (std::nothrow) dspark_ctx_kv_pack();
+  if (!p) return DSPARK_E_NOMEM;
+  const dspark_layer_desc& l0 = layers[0];
+  if (hipGetDevice(&p->device) != hipSuccess) {
+    delete p;
+    return DSPARK_E_DEVICE;
+  }
+  p->num_layers = num_layers;
+  p->hidden = hidden;
+  p->kv_size = l0.kv_size;
+  p->head_dim = l0.head_dim;
+  p->dtype = act_dtype;
+  p->has_bias = l0.qkv_bias != nullptr;
+  p->eps = (float)l0.k_norm_eps;
+  p->table = static_cast<const float*>(l0.rope_cos_sin);
+  p->table_rows = l0.rope_max_pos;
+
+  const int64_t kv2 = 2 * l0.kv_size;
+  const int64_t n_tot = num_layers * kv2;
+  int* differ = nullptr;
+  int status = DSPARK_OK;
+  auto fail = [&](int s) {
+    if (differ) (void)hipFree(differ);
+    free_pack(p);
+    return s;
+  };
+  if (hipMalloc(&p->w, (size_t)(n_tot * hidden * 2)) != hipSuccess) return fail(DSPARK_E_NOMEM);
+  if (p->has_bias && hipMalloc(&p->bias, (size_t)(n_tot * 2)) != hipSuccess)
+    return fail(DSPARK_E_NOMEM);
+  if (hipMalloc(&p->knw, (size_t)(num_layers * l0.head_dim * 4)) != hipSuccess)
+    return fail(DSPARK_E_NOMEM);
+  if (hipMalloc(&p->err, sizeof(unsigned long long)) != hipSuccess) return fail(DSPARK_E_NOMEM);
+  if (hipMalloc(&differ, sizeof(int)) != hipSuccess) return fail(DSPARK_E_NOMEM);
+
+  bool ok = true;
+  for (int32_t l = 0; l < num_layers && ok; ++l) {
+    const dspark_layer_desc& d = layers[l];
+    const uint16_t* src = static_cast<const uint16_t*>(d.qkv_weight) + d.q_size * d.w_row_stride;
+    ok &= hipMemcpy2DAsync(p->w + l * kv2 * hidden, (size_t)(hidden * 2), src,
+                           (size_t)(d.w_row_stride * 2), (size_t)(hidden * 2), (size_t)kv2,
+                           hipMemcpyDeviceToDevice, stream) == hipSuccess;
+    if (p->has_bias)
+      ok &= hipMemcpyAsync(p->bias + l * kv2, static_cast<const uint16_t*>(d.qkv_bias) + d.q_size,
+                           (size_t)(kv2 * 2), hipMemcpyDeviceToDevice, stream) == hipSuccess;
+    ok &= dspark::launch_widen_to_f32(d.k_norm_weight, d.k_norm_dtype, p->knw + l * l0.head_dim,
+                                      l0.head_dim, stream) == hipSuccess;
+  }
+  ok = ok && hipMemsetAsync(p->err, 0, sizeof(unsigned long long), stream) == hipSuccess;
+  ok = ok && hipMemsetAsync(differ, 0, sizeof(int), stream) == hipSuccess;
+  for (int32_t l = 1; l < num_layers && ok; ++l) {
+    if (layers[l].rope_cos_sin != l0.rope_cos_sin)
+      ok &= dspark::launch_compare_f32(p->table, static_cast<const float*>(layers[l].rope_cos_sin),
+                                       l0.rope_max_pos * l0.rope_dim, differ, stream) == hipSuccess;
+  }
+  int h_differ = 0;
+  ok = ok && hipMemcpyAsync(&h_differ, differ, sizeof(int), hipMemcpyDeviceToHost, stream) ==
+                 hipSuccess;
+  ok = ok && hipStreamSynchronize(stream) == hipSuccess;
+  if (!ok) return fail(DSPARK_E_DEVICE);
+  if (h_differ) {
+    status = fail(DSPARK_FALLBACK);
+    set_reason(fallback_reason, DSPARK_FB_ROPE);
+    return status;
+  }
+  (void)hipFree(differ);
+  *out = p;
+  return DSPARK_OK;
+}
+
+int dspark_ctx_kv_write(const dspark_ctx_kv_pack* p, const void* ctx_hidden, int64_t num_tokens,
+                        int64_t hidden_row_stride, const int64_t* positions, const int64_t* locs,
+                        const int64_t* commit_lens, int64_t locs_row_width, int64_t num_requests,
+                        const dspark_pool_desc* pools, int32_t num_pools, void* stream_ptr,
+                        int32_t* fallback_reason) {
+  set_reason(fallback_reason, DSPARK_FB_NONE);
+  if (!p || num_tokens < 0) return DSPARK_E_INVALID;
+  // commit_lens and the window width come together (sglang PR #31847,
+  // "fused_kv_norm_rope_write": ValueError otherwise)
+  const bool has_commit = commit_lens != nullptr;
+  if (has_commit != (locs_row_width > 0)) return DSPARK_E_INVALID;
+  if (has_commit && num_requests * locs_row_width != num_tokens) return DSPARK_E_INVALID;
+  if (!has_commit && (locs_row_width != 0 || num_requests != 0)) return DSPARK_E_INVALID;
+  if (!pools || num_pools != p->num_layers) return DSPARK_E_INVALID;
+  if (num_tokens == 0) return DSPARK_OK;
+  if (!ctx_hidden || !positions || !locs) return DSPARK_E_INVALID;
+  if (hidden_row_stride < p->hidden || hidden_row_stride % 8 != 0 ||
+      reinterpret_cast<uintptr_t>(ctx_hidden) % 16 != 0)
+    return DSPARK_E_INVALID;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return DSPARK_E_DEVICE;
+  if (dev != p->device) return DSPARK_E_INVALID;
+
+  const int64_t D = p->head_dim;
+  const int64_t NH = p->kv_size / D;
+  dspark::WriteArgs a = {};
+  for (int32_t l = 0; l < p->num_layers; ++l) {
+    const dspark_pool_desc& q = pools[l];
+    if (!q.k || !q.v || q.num_slots < 0) return DSPARK_E_INVALID;
+    const bool layout_ok =
+        q.dtype == p->dtype && q.k_stride1 == D && q.k_stride2 == 1 && q.v_stride1 == D &&
+        q.v_stride2 == 1 && q.k_stride0 >= NH * D && q.v_stride0 >= NH * D &&
+        q.k_stride0 % 8 == 0 && q.v_stride0 % 8 == 0 &&
+        reinterpret_cast<uintptr_t>(q.k) % 16 == 0 && reinterpret_cast<uintptr_t>(q.v) % 16 == 0;
+    if (!layout_ok) return fallback(fallback_reason, DSPARK_FB_POOL_LAYOUT);
+    a.pk[l] = static_cast<uint16_t*>(q.k);
+    a.pv[l] = static_cast<uint16_t*>(q.v);
+    a.ks0[l] = q.k_stride0;
+    a.vs0[l] = q.v_stride0;
+    a.slots[l] = q.num_slots;
+  }
+  a.x = static_cast<const uint16_t*>(ctx_hidden);
+  a.w = p->w;
+  a.bias = p->bias;
+  a.knw = p->knw;
+  a.table = p->table;
+  a.pos = positions;
+  a.locs = locs;
+  a.commit = commit_lens;
+  a.err = p->err;
+  a.x_stride = hidden_row_stride;
+  a.T = num_tokens;
+  a.P = p->table_rows;
+  a.W = has_commit ? locs_row_width : 1;
+  a.H = (int32_t)p->hidden;
+  a.L = p->num_layers;
+  a.NH = (int32_t)NH;
+  a.eps = p->eps;
+  const hipError_t e = dspark::launch_ctx_kv_write(a, (int)D, p->dtype == DSPARK_FP16,
+                                                   p->has_bias != 0, has_commit,
+                                                   static_cast<hipStream_t>(stream_ptr));
+  return e == hipSuccess ? DSPARK_OK : DSPARK_E_DEVICE;
+}
+
+int dspark_pack_range_errors(const dspark_ctx_kv_pack* p, void* stream_ptr, int64_t* count) {
+  if (!p || !count) return DSPARK_E_INVALID;
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  unsigned long long h = 0;
+  if (hipMemcpyAsync(&h, p->err, sizeof(h), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipMemsetAsync(p->err, 0, sizeof(h), stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return DSPARK_E_DEVICE;
+  *count = (int64_t)h;
+  return DSPARK_OK;
+}
+
+int dspark_pack_info(const dspark_ctx_kv_pack* p, int32_t* num_layers, int64_t* hidden,
+                     int64_t* kv_size, int64_t* head_dim, int32_t* act_dtype, int32_t* has_bias) {
+  if (!p) return DSPARK_E_INVALID;
+  if (num_layers) *num_layers = p->num_layers;
+  if (hidden) *hidden = p->hidden;
+  if (kv_size) *kv_size = p->kv_size;
+  if (head_dim) *head_dim = p->head_dim;
+  if (act_dtype) *act_dtype = p->dtype;
+  if (has_bias) *has_bias = p->has_bias;
+  return DSPARK_OK;
+}
+
+int dspark_pack_buffers(const dspark_ctx_kv_pack* p, const void** w_stacked, const void** bias,
+                        const float** k_norm) {
+  if (!p) return DSPARK_E_INVALID;
+  if (w_stacked) *w_stacked = p->w;
+  if (bias) *bias = p->bias;
+  if (k_norm) *k_norm = p->knw;
+  return DSPARK_OK;
+}
+
+void dspark_pack_free(dspark_ctx_kv_pack* p) {
+  if (!p) return;
+  int cur = -1;
+  (void)hipGetDevice(&cur);
+  if (cur != p->device) (void)hipSetDevice(p->device);
+  (void)hipDeviceSynchronize();
+  free_pack(p);
+  if (cur >= 0 && cur != p->device) (void)hipSetDevice(cur);
+}
+
+const char* dspark_status_str(int status) {
+  switch (status) {
+    case DSPARK_OK: return "ok";
+    case DSPARK_FALLBACK: return "fallback: not eligible for the stacked write";
+    case DSPARK_E_INVALID: return "invalid argument";
+    case DSPARK_E_DEVICE: return "HIP runtime error";
+    case DSPARK_E_NOMEM: return "device allocation failed";
+    default: return "unknown status";
+  }
+}
+
+const char* dspark_fallback_str(int reason) {
+  switch (reason) {
+    case DSPARK_FB_NONE: return "none";
+    case DSPARK_FB_NO_LAYERS: return "no layers";
+    case DSPARK_FB_TOO_MANY_LAYERS: return "more layers than DSPARK_MAX_LAYERS";
+    case DSPARK_FB_NOT_SLICEABLE: return "QKV weight cannot be sliced (quantized, other dtype or layout)";
+    case DSPARK_FB_EPS_MISMATCH: return "layers disagree on the k_norm epsilon";
+    case DSPARK_FB_MIXED_BIAS: return "QKV bias present in some layers only";
+    case DSPARK_FB_SHAPE: return "head_dim / kv_size differ or are unsupported";
+    case DSPARK_FB_DTYPE: return "unsupported activation or k_norm dtype";
+    case DSPARK_FB_KV_SCALE: return "K/V quantization scale attached";
+    case DSPARK_FB_ROPE: return "rotary is not neox full-dim over one shared fp32 table";
+    case DSPARK_FB_POOL_LAYOUT: return "KV pool dtype, layout or alignment unsupported";
+    default: return "unknown reason";
+  }
+}
+
+}  // extern "C"

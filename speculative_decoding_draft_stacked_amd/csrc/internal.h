@@ -1,0 +1,51 @@
+// Internal declarations of the HIP library (not part of the public C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dspark.h"
+
+namespace dspark {
+
+constexpr int kMaxLayers = DSPARK_MAX_LAYERS;
+
+// Everything the fused write kernel reads, passed by value in the kernel
+// arguments so that one launch can address every layer's pool.
+struct WriteArgs {
+  const uint16_t* x;        // ctx_hidden [T, H] (row stride x_stride)
+  const uint16_t* w;        // W_stacked [N_tot, H], N_tot = L * 2 * NH * D
+  const uint16_t* bias;     // [N_tot] or nullptr
+  const float* knw;         // [L, D] fp32
+  const float* table;       // [P, D] fp32: cos half | sin half
+  const int64_t* pos;       // [T]
+  const int64_t* locs;      // [T]
+  const int64_t* commit;    // [T / W] or nullptr
+  unsigned long long* err;  // range error counter
+  int64_t x_stride;
+  int64_t T;
+  int64_t P;
+  int64_t W;                // commit window width (1 when no commit_lens)
+  int32_t H;
+  int32_t L;
+  int32_t NH;
+  float eps;
+  uint16_t* pk[kMaxLayers];
+  uint16_t* pv[kMaxLayers];
+  int64_t ks0[kMaxLayers];
+  int64_t vs0[kMaxLayers];
+  int64_t slots[kMaxLayers];
+};
+
+// Launches the fused GEMM + norm + rotation + scatter for `a` on `stream`.
+// Shapes have been validated by the caller. Returns the launch status.
+hipError_t launch_ctx_kv_write(const WriteArgs& a, int head_dim, bool is_fp16, bool has_bias,
+                               bool has_commit, hipStream_t stream);
+
+// Pack helpers.
+hipError_t launch_widen_to_f32(const void* src, int dtype, float* dst, int64_t n,
+                               hipStream_t stream);
+hipError_t launch_compare_f32(const float* a, const float* b, int64_t n, int* differ,
+                              hipStream_t stream);
+
+}  // namespace dspark

@@ -1,0 +1,144 @@
+"""Host-only checks of the C ABI: the library loads, exports every function
+include/dspark.h declares, and its eligibility rules and argument checks behave
+as documented. Nothing here dereferences a device pointer or launches work."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import speculative_decoding_draft_stacked_amd as dk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "dspark.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dspark_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_documented_entry_points():
+    assert _declared() == sorted(dk.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = dk.lib()
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_struct_layouts_match_c(tmp_path):
+    """The ctypes mirrors have the C compiler's size and field offsets."""
+    fields = {"dspark_layer_desc": dk.LayerDesc, "dspark_pool_desc": dk.PoolDesc}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "dspark.h"', "int main(void) {"]
+    for cname, py in fields.items():
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    for line in out.splitlines():
+        cname, field, value = line.split()
+        py = fields[cname]
+        got = ctypes.sizeof(py) if field == "size" else getattr(py, field).offset
+        assert got == int(value), (cname, field)
+
+
+def test_status_and_reason_strings():
+    assert dk.status_str(dk.OK) == "ok"
+    assert "fallback" in dk.status_str(dk.FALLBACK)
+    assert dk.fallback_str(5) == "QKV bias present in some layers only"
+    assert dk.fallback_str(1234) == "unknown reason"
+
+
+# Fake (never dereferenced) device addresses, 16-byte aligned.
+def _layer(i=0, **kw):
+    H, D, NH = 256, 64, 2
+    base = dict(qkv_weight=0x10000000 + i * 0x100000, w_rows=H + 2 * NH * D, w_row_stride=H,
+                w_col_stride=1, w_dtype=dk.BF16, qkv_bias=None, k_norm_weight=0x20000000 + i * 256,
+                k_norm_dtype=dk.BF16, k_norm_eps=1e-6, q_size=H, kv_size=NH * D, head_dim=D,
+                has_kv_scale=0, rope_cos_sin=0x30000000, rope_dtype=dk.FP32, rope_max_pos=4096,
+                rope_dim=D, rope_is_neox=1)
+    base.update(kw)
+    return dk.LayerDesc(**base)
+
+
+def _elig(layers, hidden=256, dtype=dk.BF16):
+    return dk.check_eligibility(layers, hidden, dtype)
+
+
+def test_eligible_layers():
+    assert _elig([_layer(i) for i in range(5)]) == (dk.OK, 0)
+    assert _elig([_layer(i, qkv_bias=0x40000000 + i * 4096) for i in range(3)]) == (dk.OK, 0)
+    fp16 = [_layer(i, w_dtype=dk.FP16, k_norm_dtype=dk.FP32) for i in range(2)]
+    assert _elig(fp16, dtype=dk.FP16) == (dk.OK, 0)
+
+
+# The fallback trio of the stacked path (sglang PR #31986 parity test: quantized
+# weight, eps mismatch, bias mismatch) plus the stricter checks of the fused
+# bundle (sglang PR #31847).
+@pytest.mark.parametrize("mutate,reason", [
+    (lambda ls: ls[1].__setattr__("w_dtype", dk.QUANTIZED), "NOT_SLICEABLE"),
+    (lambda ls: ls[2].__setattr__("k_norm_eps", 1e-5), "EPS_MISMATCH"),
+    (lambda ls: ls[1].__setattr__("qkv_bias", 0x40000000), "MIXED_BIAS"),
+    (lambda ls: ls[0].__setattr__("w_col_stride", 2), "NOT_SLICEABLE"),
+    (lambda ls: ls[0].__setattr__("w_rows", 256 + 100), "NOT_SLICEABLE"),
+    (lambda ls: ls[1].__setattr__("has_kv_scale", 1), "KV_SCALE"),
+    (lambda ls: (ls[2].__setattr__("kv_size", 192), ls[2].__setattr__("w_rows", 1024)), "SHAPE"),
+    (lambda ls: [(l.__setattr__("kv_size", 96), l.__setattr__("w_rows", 1024)) for l in ls], "SHAPE"),
+    (lambda ls: ls[1].__setattr__("rope_is_neox", 0), "ROPE"),
+    (lambda ls: ls[1].__setattr__("rope_dim", 32), "ROPE"),
+    (lambda ls: ls[0].__setattr__("rope_dtype", dk.BF16), "ROPE"),
+    (lambda ls: ls[2].__setattr__("rope_max_pos", 2048), "ROPE"),
+    (lambda ls: ls[0].__setattr__("k_norm_dtype", dk.QUANTIZED), "DTYPE"),
+])
+def test_fallback_reasons(mutate, reason):
+    layers = [_layer(i) for i in range(3)]
+    mutate(layers)
+    st, r = _elig(layers)
+    assert st == dk.FALLBACK and dk.FALLBACK_REASONS[r] == reason
+
+
+def test_fallback_shapes_and_counts():
+    assert _elig([]) == (dk.FALLBACK, 1)
+    assert _elig([_layer(i) for i in range(33)])[1] == 2
+    # head_dim outside the kernels' coverage
+    l32 = [_layer(0, head_dim=32, rope_dim=32, kv_size=64)]
+    assert dk.FALLBACK_REASONS[_elig(l32)[1]] == "SHAPE"
+    # hidden not a multiple of 8
+    odd = [_layer(0, w_row_stride=260)]
+    assert dk.FALLBACK_REASONS[_elig(odd, hidden=258)[1]] == "SHAPE"
+    # activation dtype fp32 is not a supported GEMM input
+    assert dk.FALLBACK_REASONS[_elig([_layer(0)], dtype=dk.FP32)[1]] == "DTYPE"
+    # weight dtype must equal the activation dtype
+    assert dk.FALLBACK_REASONS[_elig([_layer(0)], dtype=dk.FP16)[1]] == "NOT_SLICEABLE"
+
+
+def test_invalid_arguments():
+    assert _elig([_layer(0)], hidden=0)[0] == dk.E_INVALID
+    assert _elig([_layer(0, qkv_weight=None)])[0] == dk.E_INVALID
+    lib = dk.lib()
+    assert lib.dspark_check_eligibility(None, 2, 256, dk.BF16, None) == dk.E_INVALID
+    out = ctypes.c_void_p(123)
+    # NULL out pointer, and NULL pack for every pack-taking call
+    assert lib.dspark_pack_ctx_kv(None, 1, 256, dk.BF16, None, None, None) == dk.E_INVALID
+    assert lib.dspark_ctx_kv_write(None, None, 4, 256, None, None, None, 0, 0, None, 0, None,
+                                   None) == dk.E_INVALID
+    n = ctypes.c_int64()
+    assert lib.dspark_pack_range_errors(None, None, ctypes.byref(n)) == dk.E_INVALID
+    assert lib.dspark_pack_info(None, None, None, None, None, None, None) == dk.E_INVALID
+    lib.dspark_pack_free(None)  # no-op
+    # ineligible layers: pack reports fallback before touching the device
+    reason = ctypes.c_int32()
+    arr = (dk.LayerDesc * 2)(_layer(0), _layer(1, k_norm_eps=1.0))
+    assert lib.dspark_pack_ctx_kv(arr, 2, 256, dk.BF16, None, ctypes.byref(out),
+                                  ctypes.byref(reason)) == dk.FALLBACK
+    assert out.value is None and reason.value == 4

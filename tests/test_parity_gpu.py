@@ -1,0 +1,268 @@
+"""Parity of the HIP context-KV write (through the C ABI) with the CPU oracle.
+
+Tolerance: |gpu - oracle| <= atol + rtol*|oracle| elementwise with
+(rtol, atol) = (2e-2, 2e-2) for bf16 and (5e-3, 5e-3) for fp16, the parity
+tolerances of sglang PR #31986's stacked-vs-per-layer test. Which slots are
+written is compared bit-exactly against sentinel-filled pools.
+"""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import speculative_decoding_draft_stacked_amd as dk
+from speculative_decoding_draft_stacked_amd import workloads as W
+from oracle import ctx_kv_oracle as O
+
+from gpu_util import DeviceCase, check_slot_sets, compare_rows, device_to_host, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "no GPU visible"
+    dk.lib()  # raises if the HIP library is not built
+
+
+def _run(case, label, rows=None, **kw):
+    say(f"[case] {label}: T={case.T} H={case.H} L={case.L} NH={case.NH} D={case.D} "
+        f"{case.dtype} bias={case.qkv_b is not None} W={case.row_width}")
+    dc = DeviceCase(case, **kw)
+    pack = dc.pack()
+    assert dc.write(pack)
+    torch.cuda.synchronize()
+    check_slot_sets(dc)
+    st = compare_rows(dc, rows, label)
+    assert pack.range_errors() == 0
+    say(f"  ok: {st}")
+    return dc, pack, st
+
+
+# ------------------------------------------------------------ small multi-tile cases
+
+SMALL = {
+    # ragged token tail (130 = 128 + 2), two 128-heads per layer
+    "bf16_d128_ragged_T": dict(T=130, H=320, L=2, NH=2, D=128, slots=400),
+    # odd head count: 128-row tiles straddle the K/V boundary; K tail H % 64 = 8;
+    # commit window of 7 with lengths 0..9 and 10% negative slots
+    "bf16_d64_commit_holes": dict(T=77, H=200, L=3, NH=3, D=64, row_width=7,
+                                  commit_range=(0, 9), neg_loc_frac=0.1, slots=300),
+    # fp16 with stacked bias, window 10 with lengths 0..12
+    "fp16_d128_bias_commit": dict(T=300, H=136, L=4, NH=1, D=128, dtype="fp16", bias=True,
+                                  row_width=10, commit_range=(0, 12), slots=512),
+    "fp16_d64_bias_small": dict(T=33, H=64, L=1, NH=2, D=64, dtype="fp16", bias=True, slots=40),
+    "single_row": dict(T=1, H=64, L=2, NH=1, D=128, slots=4),
+    "T32": dict(T=32, H=128, L=2, NH=2, D=64, slots=64),
+    "T513_theta1e6": dict(T=513, H=64, L=1, NH=1, D=128, slots=1024, theta=1e6, P=32768),
+    "T1000_multi_layer": dict(T=1000, H=128, L=5, NH=2, D=64, slots=2048, row_width=8),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_cases(name):
+    case = W.make_case(name=name, seed=zlib.crc32(name.encode()) % 10000, **SMALL[name])
+    _run(case, name)
+
+
+def test_k_norm_weight_fp32_and_padded_pool_rows():
+    case = W.make_case(T=50, H=96, L=2, NH=2, D=64, slots=80, seed=21)
+    _run(case, "fp32 k_norm, pool stride0 = NH*D + 16", k_norm_fp32=True, pool_row_pad=16)
+
+
+# ------------------------------------------------------------ the five workloads
+
+def _sample_rows(case, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = rng.choice(case.T, size=min(n, case.T), replace=False)
+    return np.unique(np.concatenate([rows, [0, case.T - 1]]))
+
+
+@pytest.mark.parametrize("name,sample", [
+    ("tiny", None), ("decode_commit", None), ("wide_gqa_d64", None), ("biased_fp16", 768),
+    ("prefill_8k", 384)])
+def test_workload(name, sample):
+    case = W.workload(name)
+    rows = None if sample is None else _sample_rows(case, sample, 5)
+    _, _, st = _run(case, name, rows)
+    # diagnostic only; the bar is the tolerance above
+    assert st["exact_frac"] > 0.9
+
+
+# ------------------------------------------------------------ structure and invariants
+
+def test_pack_contents():
+    """W_stacked is the layers' KV slices in layer order (K rows then V rows),
+    the bias is stacked the same way, k_norm is widened to fp32 exactly."""
+    case = W.make_case(T=8, H=64, L=3, NH=1, D=128, dtype="fp16", bias=True, seed=22, slots=16)
+    dc = DeviceCase(case)
+    pack = dc.pack()
+    info = pack.info()
+    assert info == dict(num_layers=3, hidden=64, kv_size=128, head_dim=128, act_dtype=dk.FP16,
+                        has_bias=True)
+    w_ptr, b_ptr, k_ptr = pack.buffers()
+    n_tot = case.L * 2 * case.kv
+    w = device_to_host(w_ptr, n_tot * case.H * 2).view(np.uint16).reshape(n_tot, case.H)
+    b = device_to_host(b_ptr, n_tot * 2).view(np.uint16)
+    kn = device_to_host(k_ptr, case.L * case.D * 4).view(np.float32).reshape(case.L, case.D)
+    sl = slice(case.q_size, case.q_size + 2 * case.kv)
+    assert np.array_equal(w, np.concatenate([wl[sl] for wl in case.qkv_w]))
+    assert np.array_equal(b, np.concatenate([bl[sl] for bl in case.qkv_b]))
+    want_k = np.stack([O.decode(g, "fp16") for g in case.k_norm_w]).astype(np.float32)
+    assert np.array_equal(kn, want_k)
+
+
+def test_stacked_equals_single_layer_packs():
+    """An L-layer pack writes what L one-layer packs write, bit for bit."""
+    case = W.make_case(T=70, H=128, L=3, NH=2, D=64, row_width=7, slots=128, seed=23)
+    dc, pack, _ = _run(case, "3-layer pack")
+    k_all, v_all = dc.pools_host()
+    for l in range(case.L):
+        one = W.make_case(T=70, H=128, L=1, NH=2, D=64, row_width=7, slots=128, seed=23)
+        one.qkv_w, one.k_norm_w = [case.qkv_w[l]], [case.k_norm_w[l]]
+        one.x, one.positions, one.locs, one.commit_lens = case.x, case.positions, case.locs, case.commit_lens
+        d1 = DeviceCase(one)
+        p1 = d1.pack()
+        assert d1.write(p1)
+        k1, v1 = d1.pools_host()
+        assert np.array_equal(k1[0], k_all[l]) and np.array_equal(v1[0], v_all[l])
+
+
+def test_power_of_two_scaling_on_device():
+    """No bias: X -> 2X gives exactly 2V; with eps = 0, K is bit-identical."""
+    case = W.make_case(T=40, H=128, L=2, NH=1, D=128, eps=0.0, slots=64, seed=24)
+    dc, pack, _ = _run(case, "scale x1")
+    k1, v1 = dc.pools_host()
+    case.x = O.encode(O.decode(case.x, "bf16") * 2.0, "bf16")
+    dc2 = DeviceCase(case)
+    assert dc2.write(dc2.pack())
+    k2, v2 = dc2.pools_host()
+    for l in range(case.L):
+        assert np.array_equal(k1[l], k2[l])
+        sl = case.locs
+        np.testing.assert_array_equal(O.decode(v2[l][sl], "bf16"), 2.0 * O.decode(v1[l][sl], "bf16"))
+
+
+def test_repeatable():
+    case = W.make_case(T=100, H=256, L=2, NH=2, D=128, slots=128, seed=25)
+    dc, pack, _ = _run(case, "repeat")
+    k1, v1 = dc.pools_host()
+    dc.reset_pools()
+    assert dc.write(pack)
+    k2, v2 = dc.pools_host()
+    assert all(np.array_equal(a, b) for a, b in zip(k1 + v1, k2 + v2))
+
+
+# ------------------------------------------------------------ edge cases
+
+def test_commit_len_edges():
+    """commit_len 0 writes nothing, W writes the whole row, W+3 the whole row too."""
+    case = W.make_case(T=24, H=64, L=2, NH=1, D=64, row_width=8, slots=64, seed=26)
+    case.commit_lens = np.array([0, 8, 11], dtype=np.int64)
+    dc, _, _ = _run(case, "commit 0 / W / W+3")
+    assert len(dc.touched_slots(0, "k")) == 16
+
+
+def test_all_rows_skipped_and_empty():
+    case = W.make_case(T=16, H=64, L=1, NH=1, D=64, slots=32, seed=27)
+    case.locs[:] = -1
+    dc = DeviceCase(case)
+    pack = dc.pack()
+    assert dc.write(pack)
+    assert len(dc.touched_slots(0, "k")) == 0 and len(dc.touched_slots(0, "v")) == 0
+    # T == 0: OK and nothing enqueued
+    empty = torch.empty((0, case.H), dtype=torch.bfloat16, device="cuda")
+    e64 = torch.empty((0,), dtype=torch.int64, device="cuda")
+    assert dk.ctx_kv_write(pack, empty, e64, e64, dc.pool_descs())
+    assert pack.range_errors() == 0
+
+
+def test_out_of_range_rows_are_skipped_and_counted():
+    case = W.make_case(T=20, H=64, L=2, NH=1, D=64, slots=32, P=64, seed=28)
+    case.positions[3] = 64       # == P
+    case.positions[5] = -2
+    case.locs[7] = 32            # == slots
+    dc = DeviceCase(case)
+    pack = dc.pack()
+    assert dc.write(pack)
+    torch.cuda.synchronize()
+    assert pack.range_errors() == 3 * case.L
+    assert pack.range_errors() == 0  # read-and-clear
+    skipped = {3, 5, 7}
+    want = np.sort([case.locs[t] for t in range(case.T) if t not in skipped])
+    assert np.array_equal(np.sort(dc.touched_slots(0, "k")), want)
+    ok_rows = [t for t in range(case.T) if t not in skipped]
+    compare_rows(dc, ok_rows, "out-of-range rows")
+
+
+def test_pool_layout_fallback_and_invalid_pairing():
+    case = W.make_case(T=8, H=64, L=2, NH=2, D=64, row_width=4, slots=16, seed=29)
+    dc = DeviceCase(case)
+    pack = dc.pack()
+    pools = dc.pool_descs()
+    bad = list(pools)
+    bad[1] = dk.PoolDesc(**{f: getattr(pools[1], f) for f, _ in dk.PoolDesc._fields_})
+    bad[1].k_stride1 = 2 * case.D
+    assert dk.ctx_kv_write(pack, dc.x, dc.positions, dc.locs, bad, commit_lens=dc.commit,
+                           locs_row_width=4) is False
+    wrong_dtype = list(pools)
+    wrong_dtype[0] = dk.PoolDesc(**{f: getattr(pools[0], f) for f, _ in dk.PoolDesc._fields_})
+    wrong_dtype[0].dtype = dk.FP16
+    assert dk.ctx_kv_write(pack, dc.x, dc.positions, dc.locs, wrong_dtype, commit_lens=dc.commit,
+                           locs_row_width=4) is False
+    torch.cuda.synchronize()
+    assert len(dc.touched_slots(0, "k")) == 0  # nothing written on fallback
+    raw = lambda **kw: dk.ctx_kv_write_raw(
+        pack, dc.x.data_ptr(), kw.get("T", 8), case.H, dc.positions.data_ptr(),
+        dc.locs.data_ptr(), kw.get("commit"), kw.get("W", 0), kw.get("B", 0),
+        kw.get("pools", pools), None)[0]
+    assert raw(commit=dc.commit.data_ptr()) == dk.E_INVALID               # commit without W
+    assert raw(W=4, B=2) == dk.E_INVALID                                  # W without commit
+    assert raw(commit=dc.commit.data_ptr(), W=4, B=3) == dk.E_INVALID     # B*W != T
+    assert raw(pools=pools[:1]) == dk.E_INVALID                           # wrong pool count
+    assert raw(T=-1) == dk.E_INVALID
+    with pytest.raises(ValueError):
+        dk.ctx_kv_write(pack, dc.x, dc.positions, dc.locs, pools, commit_lens=dc.commit)
+    torch.cuda.synchronize()
+    assert len(dc.touched_slots(0, "k")) == 0
+
+
+def test_rope_tables_by_content():
+    case = W.make_case(T=8, H=64, L=2, NH=1, D=64, slots=16, seed=30)
+    dc = DeviceCase(case)
+    descs = dc.layer_descs()
+    same = dc.table.clone()                       # another pointer, same content
+    descs[1] = dk.layer_desc(dc.qkv_w[1], dc.k_norm[1], case.eps, case.q_size, case.kv, case.D,
+                             same)
+    assert dk.pack_ctx_kv(descs, case.H, dk.BF16) is not None
+    other = same.clone()
+    other[5, 3] += 1e-3                           # different content
+    descs[1] = dk.layer_desc(dc.qkv_w[1], dc.k_norm[1], case.eps, case.q_size, case.kv, case.D,
+                             other)
+    assert dk.pack_ctx_kv(descs, case.H, dk.BF16) is None
+    assert dk.FALLBACK_REASONS[dk.last_fallback_reason] == "ROPE"
+
+
+def test_graph_replays_match_eager():
+    """The write captured in a HIP graph (as the benchmark times it) gives the
+    eager result on every replay, with eager work and syncs between replays."""
+    case = W.make_case(T=96, H=192, L=2, NH=2, D=128, row_width=8, slots=256, seed=31)
+    dc, pack, _ = _run(case, "eager reference")
+    k_ref, v_ref = dc.pools_host()
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    dc.reset_pools()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            assert dc.write(pack)
+    for rep in range(4):
+        for p in dc.pk + dc.pv:
+            p.view(torch.int16).fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        k, v = dc.pools_host()
+        assert all(np.array_equal(a, b) for a, b in zip(k + v, k_ref + v_ref)), rep
