@@ -11,6 +11,7 @@
 
 struct dspark_ctx_kv_pack {
   int device;
+  int num_cus;               // compute units of `device`
   int32_t num_layers;
   int64_t hidden;
   int64_t kv_size;
@@ -24,6 +25,7 @@ struct dspark_ctx_kv_pack {
   const float* table;        // [P, head_dim], caller-owned
   int64_t table_rows;
   unsigned long long* err;   // range error counter
+  uint16_t* zeros;           // 256 zero bytes read by out-of-range K lanes
 };
 
 namespace {
@@ -45,6 +47,7 @@ void free_pack(dspark_ctx_kv_pack* p) {
   if (p->bias) (void)hipFree(p->bias);
   if (p->knw) (void)hipFree(p->knw);
   if (p->err) (void)hipFree(p->err);
+  if (p->zeros) (void)hipFree(p->zeros);
   delete p;
 }
 
@@ -105,7 +108,9 @@ int dspark_pack_ctx_kv(const dspark_layer_desc* layers, int32_t num_layers, int6
   dspark_ctx_kv_pack* p = new (std::nothrow) dspark_ctx_kv_pack();
   if (!p) return DSPARK_E_NOMEM;
   const dspark_layer_desc& l0 = layers[0];
-  if (hipGetDevice(&p->device) != hipSuccess) {
+  if (hipGetDevice(&p->device) != hipSuccess ||
+      hipDeviceGetAttribute(&p->num_cus, hipDeviceAttributeMultiprocessorCount, p->device) !=
+          hipSuccess) {
     delete p;
     return DSPARK_E_DEVICE;
   }
@@ -134,6 +139,7 @@ int dspark_pack_ctx_kv(const dspark_layer_desc* layers, int32_t num_layers, int6
   if (hipMalloc(&p->knw, (size_t)(num_layers * l0.head_dim * 4)) != hipSuccess)
     return fail(DSPARK_E_NOMEM);
   if (hipMalloc(&p->err, sizeof(unsigned long long)) != hipSuccess) return fail(DSPARK_E_NOMEM);
+  if (hipMalloc(&p->zeros, 256) != hipSuccess) return fail(DSPARK_E_NOMEM);
   if (hipMalloc(&differ, sizeof(int)) != hipSuccess) return fail(DSPARK_E_NOMEM);
 
   bool ok = true;
@@ -150,6 +156,7 @@ int dspark_pack_ctx_kv(const dspark_layer_desc* layers, int32_t num_layers, int6
                                       l0.head_dim, stream) == hipSuccess;
   }
   ok = ok && hipMemsetAsync(p->err, 0, sizeof(unsigned long long), stream) == hipSuccess;
+  ok = ok && hipMemsetAsync(p->zeros, 0, 256, stream) == hipSuccess;
   ok = ok && hipMemsetAsync(differ, 0, sizeof(int), stream) == hipSuccess;
   for (int32_t l = 1; l < num_layers && ok; ++l) {
     if (layers[l].rope_cos_sin != l0.rope_cos_sin)
@@ -216,6 +223,7 @@ int dspark_ctx_kv_write(const dspark_ctx_kv_pack* p, const void* ctx_hidden, int
   a.w = p->w;
   a.bias = p->bias;
   a.knw = p->knw;
+  a.zeros = p->zeros;
   a.table = p->table;
   a.pos = positions;
   a.locs = locs;
@@ -230,7 +238,7 @@ int dspark_ctx_kv_write(const dspark_ctx_kv_pack* p, const void* ctx_hidden, int
   a.NH = (int32_t)NH;
   a.eps = p->eps;
   const hipError_t e = dspark::launch_ctx_kv_write(a, (int)D, p->dtype == DSPARK_FP16,
-                                                   p->has_bias != 0, has_commit,
+                                                   p->has_bias != 0, has_commit, p->num_cus,
                                                    static_cast<hipStream_t>(stream_ptr));
   return e == hipSuccess ? DSPARK_OK : DSPARK_E_DEVICE;
 }

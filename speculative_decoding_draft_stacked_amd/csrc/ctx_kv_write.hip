@@ -71,6 +71,24 @@ struct Elem<true> {  // fp16
   }
 };
 
+// 16-byte load through a global-address-space pointer: the compiler emits
+// global_load (counted by vmcnt only) rather than flat_load, which would also
+// hold up every LDS wait behind outstanding memory loads.
+__device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
+  const u32x4 v = *(global_u32x4*)p;
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS accesses,
+// not for its outstanding global loads, so prefetches stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <typename E>
 __device__ __forceinline__ void unpack8(const uint4& u, float* f) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
@@ -89,145 +107,15 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-template <bool FP16, int D, bool BIAS, bool COMMIT, int BT, int WAVES_N>
-__global__ __launch_bounds__(NTHREADS) void ctx_kv_write_kernel(const WriteArgs a) {
-  using E = Elem<FP16>;
-  using vec8 = typename E::vec8;
-  constexpr int WAVES_T = 4 / WAVES_N;
-  constexpr int MB = BN / 32 / WAVES_N;  // 32-row blocks per wave
-  constexpr int NB = BT / 32 / WAVES_T;  // 32-token blocks per wave
-  constexpr int CPR = BK / 8;            // 16-byte chunks per operand row slice
-  constexpr int W_CHUNKS = BN * CPR / NTHREADS;
-  constexpr int X_CHUNKS = BT * CPR / NTHREADS;
-  static_assert(MB >= 1 && NB >= 1 && W_CHUNKS >= 1 && X_CHUNKS >= 1, "tile shape");
-  static_assert(BN % D == 0, "a tile holds whole heads");
-
-  constexpr int SW = BN * LDK;
-  constexpr int SX = BT * LDK;
-  constexpr int LDO = BN + 4;  // output tile row: 264 bytes, 8-byte aligned rows
-  constexpr int OPER = 2 * (SW + SX);
-  constexpr int OUT = BT * LDO;
-  __shared__ __align__(16) uint16_t smem[OPER > OUT ? OPER : OUT];
-  uint16_t* sW = smem;
-  uint16_t* sX = smem + 2 * SW;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wave_n = wave / WAVES_T;
-  const int wave_t = wave % WAVES_T;
-
+// Epilogue shared by both kernels: from the dtype-rounded LDS tile [BT][LDO]
+// (tokens x the tile's 128 weight rows), normalise + rotate each K head, copy
+// each V head, and scatter both into the token's slot of the head's layer pool.
+// Each (token, head) is handled by D/16 lanes; lane j owns elements
+// [8j, 8j+8) of the first half and their rotation partners 8j + D/2 + [0, 8).
+template <typename E, int D, int BT, bool COMMIT, int LDO>
+__device__ __forceinline__ void scatter_tile(const WriteArgs& a, const uint16_t* sO, int64_t n0,
+                                             int64_t t0, int tid) {
   const int64_t T = a.T;
-  const int H = a.H;
-  const int64_t t_tiles = (T + BT - 1) / BT;
-  const int64_t bid = blockIdx.x;
-  const int64_t t_blk = bid % t_tiles;
-  const int64_t n_blk = bid / t_tiles;
-  const int64_t n0 = n_blk * BN;
-  const int64_t t0 = t_blk * BT;
-  const int nk = (H + BK - 1) / BK;
-
-  uint4 rw[W_CHUNKS];
-  uint4 rx[X_CHUNKS];
-  const uint4 zero = make_uint4(0, 0, 0, 0);
-
-  auto load = [&](int kt) {
-    const int k0 = kt * BK;
-#pragma unroll
-    for (int i = 0; i < W_CHUNKS; ++i) {
-      const int c = tid + i * NTHREADS;
-      const int row = c / CPR;
-      const int k = k0 + (c % CPR) * 8;
-      rw[i] = (k < H) ? *reinterpret_cast<const uint4*>(a.w + (n0 + row) * (int64_t)H + k) : zero;
-    }
-#pragma unroll
-    for (int i = 0; i < X_CHUNKS; ++i) {
-      const int c = tid + i * NTHREADS;
-      const int row = c / CPR;
-      const int k = k0 + (c % CPR) * 8;
-      const int64_t t = t0 + row;
-      rx[i] = (k < H && t < T) ? *reinterpret_cast<const uint4*>(a.x + t * a.x_stride + k) : zero;
-    }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < W_CHUNKS; ++i) {
-      const int c = tid + i * NTHREADS;
-      *reinterpret_cast<uint4*>(sW + buf * SW + (c / CPR) * LDK + (c % CPR) * 8) = rw[i];
-    }
-#pragma unroll
-    for (int i = 0; i < X_CHUNKS; ++i) {
-      const int c = tid + i * NTHREADS;
-      *reinterpret_cast<uint4*>(sX + buf * SX + (c / CPR) * LDK + (c % CPR) * 8) = rx[i];
-    }
-  };
-
-  f32x16 acc[MB][NB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
-
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load(kt + 1);
-    const uint16_t* cw = sW + cur * SW;
-    const uint16_t* cx = sX + cur * SX;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      // lane l supplies row (l % 32) and the 8 consecutive k at 8 * (l / 32)
-      const int kof = kk * 16 + (lane >> 5) * 8;
-      vec8 af[MB], bfr[NB];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        af[mb] = *reinterpret_cast<const vec8*>(
-            cw + (wave_n * MB * 32 + mb * 32 + (lane & 31)) * LDK + kof);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        bfr[nb] = *reinterpret_cast<const vec8*>(
-            cx + (wave_t * NB * 32 + nb * 32 + (lane & 31)) * LDK + kof);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = E::mfma(af[mb], bfr[nb], acc[mb][nb]);
-    }
-    if (kt + 1 < nk) store(cur ^ 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue 1: accumulators (+ bias) -> dtype, into the LDS tile [BT][LDO].
-  // 32x32 accumulator layout: lane l holds column (token) l % 32 and, in
-  // register r, row 8 * (r / 4) + 4 * (l / 32) + r % 4.
-  uint16_t* sO = smem;
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int tok = wave_t * NB * 32 + nb * 32 + (lane & 31);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = wave_n * MB * 32 + mb * 32 + 8 * q + 4 * (lane >> 5);
-        float v[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[i] = acc[mb][nb][4 * q + i];
-          if (BIAS) v[i] += E::to_f(a.bias[n0 + row + i]);
-        }
-        uint2 packed;
-        packed.x = E::from_f(v[0]) | (E::from_f(v[1]) << 16);
-        packed.y = E::from_f(v[2]) | (E::from_f(v[3]) << 16);
-        *reinterpret_cast<uint2*>(sO + tok * LDO + row) = packed;
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- epilogue 2: per (token, head): norm + rotation for K, copy for V, scatter.
   constexpr int TPH = D / 16;  // lanes per (token, head)
   constexpr int HPT = BN / D;  // heads per tile
   constexpr int ROUNDS = BT * HPT * TPH / NTHREADS;
@@ -293,49 +181,349 @@ __global__ __launch_bounds__(NTHREADS) void ctx_kv_write_kernel(const WriteArgs 
 }
 
 template <bool FP16, int D, bool BIAS, bool COMMIT, int BT, int WAVES_N>
-hipError_t launch_tile(const WriteArgs& a, hipStream_t stream) {
+__global__ __launch_bounds__(NTHREADS) void ctx_kv_write_kernel(const WriteArgs a) {
+  using E = Elem<FP16>;
+  using vec8 = typename E::vec8;
+  constexpr int WAVES_T = 4 / WAVES_N;
+  constexpr int MB = BN / 32 / WAVES_N;  // 32-row blocks per wave
+  constexpr int NB = BT / 32 / WAVES_T;  // 32-token blocks per wave
+  constexpr int CPR = BK / 8;            // 16-byte chunks per operand row slice
+  constexpr int W_CHUNKS = BN * CPR / NTHREADS;
+  constexpr int X_CHUNKS = BT * CPR / NTHREADS;
+  static_assert(MB >= 1 && NB >= 1 && W_CHUNKS >= 1 && X_CHUNKS >= 1, "tile shape");
+  static_assert(BN % D == 0, "a tile holds whole heads");
+
+  constexpr int SW = BN * LDK;
+  constexpr int SX = BT * LDK;
+  constexpr int LDO = BN + 4;  // output tile row: 264 bytes, 8-byte aligned rows
+  constexpr int OPER = 2 * (SW + SX);
+  constexpr int OUT = BT * LDO;
+  __shared__ __align__(16) uint16_t smem[OPER > OUT ? OPER : OUT];
+  uint16_t* sW = smem;
+  uint16_t* sX = smem + 2 * SW;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wave_n = wave / WAVES_T;
+  const int wave_t = wave % WAVES_T;
+
+  const int64_t T = a.T;
+  const int H = a.H;
+  const int64_t t_tiles = (T + BT - 1) / BT;
+  const int64_t bid = blockIdx.x;
+  const int64_t t_blk = bid % t_tiles;
+  const int64_t n_blk = bid / t_tiles;
+  const int64_t n0 = n_blk * BN;
+  const int64_t t0 = t_blk * BT;
+  const int nk = (H + BK - 1) / BK;
+
+  uint4 rw[W_CHUNKS];
+  uint4 rx[X_CHUNKS];
+
+  auto load = [&](int kt) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < W_CHUNKS; ++i) {
+      const int c = tid + i * NTHREADS;
+      const int row = c / CPR;
+      const int k = k0 + (c % CPR) * 8;
+      rw[i] = ldg16(k < H ? a.w + (n0 + row) * (int64_t)H + k : a.zeros);
+    }
+#pragma unroll
+    for (int i = 0; i < X_CHUNKS; ++i) {
+      const int c = tid + i * NTHREADS;
+      const int row = c / CPR;
+      const int k = k0 + (c % CPR) * 8;
+      const int64_t t = t0 + row < T ? t0 + row : T - 1;  // rows past T are never stored
+      rx[i] = ldg16(k < H ? a.x + t * a.x_stride + k : a.zeros);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < W_CHUNKS; ++i) {
+      const int c = tid + i * NTHREADS;
+      *reinterpret_cast<uint4*>(sW + buf * SW + (c / CPR) * LDK + (c % CPR) * 8) = rw[i];
+    }
+#pragma unroll
+    for (int i = 0; i < X_CHUNKS; ++i) {
+      const int c = tid + i * NTHREADS;
+      *reinterpret_cast<uint4*>(sX + buf * SX + (c / CPR) * LDK + (c % CPR) * 8) = rx[i];
+    }
+  };
+
+  f32x16 acc[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
+
+  load(0);
+  store(0);
+  lds_barrier();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    load(kt + 1);  // past the last slice this reads the zero page
+    const uint16_t* cw = sW + cur * SW;
+    const uint16_t* cx = sX + cur * SX;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      // lane l supplies row (l % 32) and the 8 consecutive k at 8 * (l / 32)
+      const int kof = kk * 16 + (lane >> 5) * 8;
+      vec8 af[MB], bfr[NB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        af[mb] = *reinterpret_cast<const vec8*>(
+            cw + (wave_n * MB * 32 + mb * 32 + (lane & 31)) * LDK + kof);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        bfr[nb] = *reinterpret_cast<const vec8*>(
+            cx + (wave_t * NB * 32 + nb * 32 + (lane & 31)) * LDK + kof);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = E::mfma(af[mb], bfr[nb], acc[mb][nb]);
+    }
+    store(cur ^ 1);
+    lds_barrier();
+  }
+
+  // ---- epilogue 1: accumulators (+ bias) -> dtype, into the LDS tile [BT][LDO].
+  // 32x32 accumulator layout: lane l holds column (token) l % 32 and, in
+  // register r, row 8 * (r / 4) + 4 * (l / 32) + r % 4.
+  uint16_t* sO = smem;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int tok = wave_t * NB * 32 + nb * 32 + (lane & 31);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = wave_n * MB * 32 + mb * 32 + 8 * q + 4 * (lane >> 5);
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[i] = acc[mb][nb][4 * q + i];
+          if (BIAS) v[i] += E::to_f(a.bias[n0 + row + i]);
+        }
+        uint2 packed;
+        packed.x = E::from_f(v[0]) | (E::from_f(v[1]) << 16);
+        packed.y = E::from_f(v[2]) | (E::from_f(v[3]) << 16);
+        *reinterpret_cast<uint2*>(sO + tok * LDO + row) = packed;
+      }
+    }
+  }
+  __syncthreads();
+
+  scatter_tile<E, D, BT, COMMIT, LDO>(a, sO, n0, t0, tid);
+}
+
+// Weight-streaming kernel for small T (decode-sized batches). A workgroup owns
+// one 128-row tile of the stacked weight and BT = 32*NB tokens; the host picks
+// the number of token splits so that the whole grid is one round of
+// workgroups. Wave w owns weight rows [32w, 32w+32) of the tile and streams
+// them from HBM straight into a PF-deep register ring (no LDS): for a 64-wide
+// K chunk, lane l holds row l % 32 and the 32 contiguous k at 32*(l / 32).
+// The K order inside a chunk is permuted to match: MFMA step kk takes, in lane
+// half h, k = 32h + 8kk + [0, 8), and the X operand is read from LDS with the
+// same permutation (a sum over k does not depend on its order). X chunks
+// travel through a register ring of the same depth into double-buffered LDS,
+// so every wait on an X load also only waits for weight loads of the same
+// chunk (loads complete in issue order).
+template <bool FP16, int D, bool BIAS, bool COMMIT, int NB, int PF>
+__global__ __launch_bounds__(NTHREADS) void ctx_kv_stream_kernel(const WriteArgs a, int splits) {
+  using E = Elem<FP16>;
+  using vec8 = typename E::vec8;
+  static_assert(PF % 2 == 0, "the LDS double buffer is indexed by ring slot parity");
+  constexpr int BT = 32 * NB;
+  constexpr int XC = BT * (BK / 8) / NTHREADS;  // 16-byte X pieces per thread per chunk
+  static_assert(XC * NTHREADS == BT * (BK / 8), "X chunk split");
+  constexpr int LDX = BK + 8;
+  constexpr int SXS = BT * LDX;
+  constexpr int LDO = BN + 4;
+  constexpr int OPER = 2 * SXS;
+  constexpr int OUT = BT * LDO;
+  __shared__ __align__(16) uint16_t smem[OPER > OUT ? OPER : OUT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r32 = lane & 31;
+  const int hh = lane >> 5;
+  const int64_t T = a.T;
+  const int H = a.H;
+  const int64_t R = (int64_t)a.L * 2 * a.NH * D / BN;
+  // Workgroup b runs on XCD b % 8. When the row tiles divide evenly, the
+  // `splits` workgroups sharing a weight tile are placed on one XCD and
+  // dispatched back to back, so its L2 serves the tile to all of them.
+  const int64_t b = blockIdx.x;
+  int64_t rt, sp;
+  if (R % 8 == 0) {
+    const int64_t i = b / 8;
+    rt = 8 * (i / splits) + b % 8;
+    sp = i % splits;
+  } else {
+    rt = b / splits;
+    sp = b % splits;
+  }
+  const int64_t n0 = rt * BN;
+  const int64_t t0 = sp * BT;
+  const int nk = (H + BK - 1) / BK;
+  const uint16_t* wrow = a.w + (n0 + 32 * wave + r32) * (int64_t)H + 32 * hh;
+
+  uint4 wq[PF][4];
+  uint4 rx[PF][XC];
+  auto load_chunk = [&](int c, uint4(&wd)[4], uint4(&xd)[XC]) {
+    const int k0 = c * BK;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = k0 + 32 * hh + 8 * j;
+      wd[j] = ldg16(k < H ? wrow + k0 + 8 * j : a.zeros);
+    }
+#pragma unroll
+    for (int i = 0; i < XC; ++i) {
+      const int e = tid + i * NTHREADS;
+      const int64_t t = t0 + e / 8 < T ? t0 + e / 8 : T - 1;  // rows past T are never stored
+      const int k = k0 + (e % 8) * 8;
+      xd[i] = ldg16(k < H ? a.x + t * a.x_stride + k : a.zeros);
+    }
+  };
+  auto stage_x = [&](int buf, const uint4(&xd)[XC]) {
+#pragma unroll
+    for (int i = 0; i < XC; ++i) {
+      const int e = tid + i * NTHREADS;
+      *reinterpret_cast<uint4*>(smem + buf * SXS + (e / 8) * LDX + (e % 8) * 8) = xd[i];
+    }
+  };
+
+  f32x16 acc[NB];
+#pragma unroll
+  for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[tb][r] = 0.0f;
+
+  // The loop runs a whole number of ring turns with no branches, so the
+  // compiler's load counters stay exact; chunks past the end read the zero
+  // page and add nothing.
+  const int nk_ring = (nk + PF - 1) / PF * PF;
+#pragma unroll
+  for (int s = 0; s < PF; ++s) load_chunk(s, wq[s], rx[s]);
+  stage_x(0, rx[0]);
+  lds_barrier();
+
+  for (int c0 = 0; c0 < nk_ring; c0 += PF) {
+#pragma unroll
+    for (int s = 0; s < PF; ++s) {
+      const int c = c0 + s;
+      const uint16_t* xs = smem + (s & 1) * SXS;  // chunk c sits in buffer c & 1 == s & 1
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        const vec8 av = __builtin_bit_cast(vec8, wq[s][kk]);
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) {
+          const vec8 bv =
+              *reinterpret_cast<const vec8*>(xs + (tb * 32 + r32) * LDX + 32 * hh + 8 * kk);
+          acc[tb] = E::mfma(av, bv, acc[tb]);
+        }
+      }
+      stage_x((s + 1) & 1, rx[(s + 1) % PF]);
+      load_chunk(c + PF, wq[s], rx[s]);
+      lds_barrier();
+    }
+  }
+
+  // accumulators (+ bias) -> dtype, into the LDS tile [BT][LDO]
+  uint16_t* sO = smem;
+#pragma unroll
+  for (int tb = 0; tb < NB; ++tb) {
+    const int tok = tb * 32 + r32;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = 32 * wave + 8 * q + 4 * hh;
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[i] = acc[tb][4 * q + i];
+        if (BIAS) v[i] += E::to_f(a.bias[n0 + row + i]);
+      }
+      uint2 packed;
+      packed.x = E::from_f(v[0]) | (E::from_f(v[1]) << 16);
+      packed.y = E::from_f(v[2]) | (E::from_f(v[3]) << 16);
+      *reinterpret_cast<uint2*>(sO + tok * LDO + row) = packed;
+    }
+  }
+  __syncthreads();
+  scatter_tile<E, D, BT, COMMIT, LDO>(a, sO, n0, t0, tid);
+}
+
+template <bool FP16, int D, bool BIAS, bool COMMIT>
+hipError_t launch_tiled(const WriteArgs& a, hipStream_t stream) {
+  constexpr int BT = 128;
   const int64_t n_tiles = (int64_t)a.L * 2 * a.NH * D / BN;
-  const int64_t t_tiles = (a.T + BT - 1) / BT;
-  const int64_t grid = n_tiles * t_tiles;
+  const int64_t grid = n_tiles * ((a.T + BT - 1) / BT);
   if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((ctx_kv_write_kernel<FP16, D, BIAS, COMMIT, BT, WAVES_N>), dim3((uint32_t)grid),
+  hipLaunchKernelGGL((ctx_kv_write_kernel<FP16, D, BIAS, COMMIT, BT, 2>), dim3((uint32_t)grid),
                      dim3(NTHREADS), 0, stream, a);
   return hipGetLastError();
 }
 
+template <bool FP16, int D, bool BIAS, bool COMMIT, int NB>
+hipError_t launch_stream_nb(const WriteArgs& a, int64_t row_tiles, int splits, hipStream_t stream) {
+  constexpr int PF = NB == 1 ? 8 : (NB == 4 ? 4 : 6);
+  hipLaunchKernelGGL((ctx_kv_stream_kernel<FP16, D, BIAS, COMMIT, NB, PF>),
+                     dim3((uint32_t)(row_tiles * splits)), dim3(NTHREADS), 0, stream, a, splits);
+  return hipGetLastError();
+}
+
+// Small T: one round of streaming workgroups (row tiles x token splits of up
+// to 4 blocks of 32 tokens) fits on the device. Larger T: LDS-tiled kernel.
 template <bool FP16, int D, bool BIAS, bool COMMIT>
-hipError_t launch_by_rows(const WriteArgs& a, hipStream_t stream) {
-  if (a.T <= 32) return launch_tile<FP16, D, BIAS, COMMIT, 32, 4>(a, stream);
-  if (a.T <= 512) return launch_tile<FP16, D, BIAS, COMMIT, 64, 2>(a, stream);
-  return launch_tile<FP16, D, BIAS, COMMIT, 128, 2>(a, stream);
+hipError_t launch_by_rows(const WriteArgs& a, int num_cus, hipStream_t stream) {
+  const int64_t row_tiles = (int64_t)a.L * 2 * a.NH * D / BN;
+  const int64_t blocks = (a.T + 31) / 32;
+  const int64_t cap = row_tiles >= num_cus ? 1 : num_cus / row_tiles;
+  if (blocks > 4 * cap) return launch_tiled<FP16, D, BIAS, COMMIT>(a, stream);
+  int64_t splits = blocks < cap ? blocks : cap;
+  const int64_t nb = (blocks + splits - 1) / splits;
+  splits = (blocks + nb - 1) / nb;
+  switch (nb) {
+    case 1: return launch_stream_nb<FP16, D, BIAS, COMMIT, 1>(a, row_tiles, (int)splits, stream);
+    case 2: return launch_stream_nb<FP16, D, BIAS, COMMIT, 2>(a, row_tiles, (int)splits, stream);
+    case 3: return launch_stream_nb<FP16, D, BIAS, COMMIT, 3>(a, row_tiles, (int)splits, stream);
+    default: return launch_stream_nb<FP16, D, BIAS, COMMIT, 4>(a, row_tiles, (int)splits, stream);
+  }
 }
 
 template <bool FP16, int D, bool BIAS>
-hipError_t launch_commit(const WriteArgs& a, bool has_commit, hipStream_t stream) {
-  return has_commit ? launch_by_rows<FP16, D, BIAS, true>(a, stream)
-                    : launch_by_rows<FP16, D, BIAS, false>(a, stream);
+hipError_t launch_commit(const WriteArgs& a, bool has_commit, int num_cus, hipStream_t stream) {
+  return has_commit ? launch_by_rows<FP16, D, BIAS, true>(a, num_cus, stream)
+                    : launch_by_rows<FP16, D, BIAS, false>(a, num_cus, stream);
 }
 
 template <bool FP16, int D>
-hipError_t launch_bias(const WriteArgs& a, bool has_bias, bool has_commit, hipStream_t stream) {
-  return has_bias ? launch_commit<FP16, D, true>(a, has_commit, stream)
-                  : launch_commit<FP16, D, false>(a, has_commit, stream);
+hipError_t launch_bias(const WriteArgs& a, bool has_bias, bool has_commit, int num_cus,
+                       hipStream_t stream) {
+  return has_bias ? launch_commit<FP16, D, true>(a, has_commit, num_cus, stream)
+                  : launch_commit<FP16, D, false>(a, has_commit, num_cus, stream);
 }
 
 template <bool FP16>
 hipError_t launch_dim(const WriteArgs& a, int head_dim, bool has_bias, bool has_commit,
-                      hipStream_t stream) {
-  if (head_dim == 128) return launch_bias<FP16, 128>(a, has_bias, has_commit, stream);
-  if (head_dim == 64) return launch_bias<FP16, 64>(a, has_bias, has_commit, stream);
+                      int num_cus, hipStream_t stream) {
+  if (head_dim == 128) return launch_bias<FP16, 128>(a, has_bias, has_commit, num_cus, stream);
+  if (head_dim == 64) return launch_bias<FP16, 64>(a, has_bias, has_commit, num_cus, stream);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_ctx_kv_write(const WriteArgs& a, int head_dim, bool is_fp16, bool has_bias,
-                               bool has_commit, hipStream_t stream) {
-  return is_fp16 ? launch_dim<true>(a, head_dim, has_bias, has_commit, stream)
-                 : launch_dim<false>(a, head_dim, has_bias, has_commit, stream);
+                               bool has_commit, int num_cus, hipStream_t stream) {
+  if (num_cus < 1) num_cus = 1;
+  return is_fp16 ? launch_dim<true>(a, head_dim, has_bias, has_commit, num_cus, stream)
+                 : launch_dim<false>(a, head_dim, has_bias, has_commit, num_cus, stream);
 }
 
 }  // namespace dspark

@@ -17,6 +17,7 @@ struct WriteArgs {
   const uint16_t* w;        // W_stacked [N_tot, H], N_tot = L * 2 * NH * D
   const uint16_t* bias;     // [N_tot] or nullptr
   const float* knw;         // [L, D] fp32
+  const uint16_t* zeros;    // 16 zero bytes: the source of K-tail lanes past H
   const float* table;       // [P, D] fp32: cos half | sin half
   const int64_t* pos;       // [T]
   const int64_t* locs;      // [T]
@@ -38,9 +39,10 @@ struct WriteArgs {
 };
 
 // Launches the fused GEMM + norm + rotation + scatter for `a` on `stream`.
-// Shapes have been validated by the caller. Returns the launch status.
+// `num_cus` (compute units of the device) sizes the small-T grid. Shapes have
+// been validated by the caller. Returns the launch status.
 hipError_t launch_ctx_kv_write(const WriteArgs& a, int head_dim, bool is_fp16, bool has_bias,
-                               bool has_commit, hipStream_t stream);
+                               bool has_commit, int num_cus, hipStream_t stream);
 
 // Pack helpers.
 hipError_t launch_widen_to_f32(const void* src, int dtype, float* dst, int64_t n,
