@@ -178,8 +178,15 @@ int dspark_pack_info(const dspark_ctx_kv_pack* pack, int32_t* num_layers, int64_
                      int64_t* kv_size, int64_t* head_dim, int32_t* act_dtype,
                      int32_t* has_bias);
 
-/* Device pointers of the pack's stacked weight [L*2*kv, hidden], bias (NULL if
- * none) and fp32 k_norm [L, head_dim], for inspection. Owned by the pack. */
+/* Device pointers of the pack's stacked weight, bias (NULL if none) and fp32
+ * k_norm [L, head_dim], for inspection. Owned by the pack.
+ * The bias is [L*2*kv] in stacking order. The stacked weight [L*2*kv, hidden]
+ * (layer-major, K rows then V rows) is stored in the library's blocked
+ * layout: with nk = ceil(hidden / 64), block (rt, c) for row tile rt (rows
+ * [128 rt, 128 rt + 128)) and column chunk c (columns [64 c, 64 c + 64)) is
+ * 1024 pieces of 8 elements starting at element ((rt * nk + c) * 1024) * 8;
+ * piece q = (g * 4 + s) * 64 + l holds row 128 rt + 32 g + (l % 32), columns
+ * 64 c + 32 (l / 32) + 8 s + [0, 8). Columns at or past `hidden` are zero. */
 int dspark_pack_buffers(const dspark_ctx_kv_pack* pack, const void** w_stacked,
                         const void** bias, const float** k_norm);
 

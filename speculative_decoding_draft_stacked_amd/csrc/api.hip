@@ -19,7 +19,7 @@ struct dspark_ctx_kv_pack {
   int32_t dtype;
   int32_t has_bias;
   float eps;
-  uint16_t* w;               // [L * 2 * kv, hidden]
+  uint16_t* w;               // [L * 2 * kv, hidden] in the blocked layout
   uint16_t* bias;            // [L * 2 * kv] or nullptr
   float* knw;                // [L, head_dim]
   const float* table;        // [P, head_dim], caller-owned
@@ -126,14 +126,18 @@ int dspark_pack_ctx_kv(const dspark_layer_desc* layers, int32_t num_layers, int6
 
   const int64_t kv2 = 2 * l0.kv_size;
   const int64_t n_tot = num_layers * kv2;
+  const int64_t nk = (hidden + 63) / 64;
   int* differ = nullptr;
+  uint16_t* plain = nullptr;
   int status = DSPARK_OK;
   auto fail = [&](int s) {
     if (differ) (void)hipFree(differ);
+    if (plain) (void)hipFree(plain);
     free_pack(p);
     return s;
   };
-  if (hipMalloc(&p->w, (size_t)(n_tot * hidden * 2)) != hipSuccess) return fail(DSPARK_E_NOMEM);
+  if (hipMalloc(&p->w, (size_t)(n_tot * nk * 64 * 2)) != hipSuccess) return fail(DSPARK_E_NOMEM);
+  if (hipMalloc(&plain, (size_t)(n_tot * hidden * 2)) != hipSuccess) return fail(DSPARK_E_NOMEM);
   if (p->has_bias && hipMalloc(&p->bias, (size_t)(n_tot * 2)) != hipSuccess)
     return fail(DSPARK_E_NOMEM);
   if (hipMalloc(&p->knw, (size_t)(num_layers * l0.head_dim * 4)) != hipSuccess)
@@ -146,7 +150,7 @@ int dspark_pack_ctx_kv(const dspark_layer_desc* layers, int32_t num_layers, int6
   for (int32_t l = 0; l < num_layers && ok; ++l) {
     const dspark_layer_desc& d = layers[l];
     const uint16_t* src = static_cast<const uint16_t*>(d.qkv_weight) + d.q_size * d.w_row_stride;
-    ok &= hipMemcpy2DAsync(p->w + l * kv2 * hidden, (size_t)(hidden * 2), src,
+    ok &= hipMemcpy2DAsync(plain + l * kv2 * hidden, (size_t)(hidden * 2), src,
                            (size_t)(d.w_row_stride * 2), (size_t)(hidden * 2), (size_t)kv2,
                            hipMemcpyDeviceToDevice, stream) == hipSuccess;
     if (p->has_bias)
@@ -155,6 +159,7 @@ int dspark_pack_ctx_kv(const dspark_layer_desc* layers, int32_t num_layers, int6
     ok &= dspark::launch_widen_to_f32(d.k_norm_weight, d.k_norm_dtype, p->knw + l * l0.head_dim,
                                       l0.head_dim, stream) == hipSuccess;
   }
+  ok = ok && dspark::launch_block_weight(plain, n_tot, hidden, p->w, stream) == hipSuccess;
   ok = ok && hipMemsetAsync(p->err, 0, sizeof(unsigned long long), stream) == hipSuccess;
   ok = ok && hipMemsetAsync(p->zeros, 0, 256, stream) == hipSuccess;
   ok = ok && hipMemsetAsync(differ, 0, sizeof(int), stream) == hipSuccess;
@@ -174,6 +179,7 @@ int dspark_pack_ctx_kv(const dspark_layer_desc* layers, int32_t num_layers, int6
     return status;
   }
   (void)hipFree(differ);
+  (void)hipFree(plain);
   *out = p;
   return DSPARK_OK;
 }

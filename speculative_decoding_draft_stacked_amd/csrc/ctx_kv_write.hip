@@ -180,75 +180,106 @@ __device__ __forceinline__ void scatter_tile(const WriteArgs& a, const uint16_t*
   }
 }
 
-template <bool FP16, int D, bool BIAS, bool COMMIT, int BT, int WAVES_N>
-__global__ __launch_bounds__(NTHREADS) void ctx_kv_write_kernel(const WriteArgs a) {
+// 16-byte direct-to-LDS load (gfx950 global_load_lds_dwordx4): lane i of the
+// wave writes its 16 bytes to lds_wave_base + 16 * i; lds_wave_base must be
+// the same for the whole wave.
+__device__ __forceinline__ void ldg16_to_lds(const uint16_t* src, uint16_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                   (void __attribute__((address_space(3)))*)lds_wave_base, 16, 0,
+                                   0);
+}
+
+// Plain workgroup barrier. The caller has already waited (vmcnt) for its own
+// direct-to-LDS loads; a fence here would wait for all of them, including the
+// prefetches that must stay in flight. The memory clobber keeps the compiler
+// from moving LDS accesses across it.
+__device__ __forceinline__ void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// LDS-tiled kernel for large T. A workgroup owns one 128-row weight tile and
+// BT = 256 tokens; its 4 waves form a 2 x 2 grid of 64-row x 128-token wave
+// tiles (2 x 4 MFMA blocks each). Every 64-wide K chunk is brought into one of
+// three LDS stages by direct-to-LDS loads, two chunks ahead of the MFMAs, with
+// no register staging:
+//   - the chunk's weight block is copied linearly (the blocked layout already
+//     puts each wave's A fragment for one MFMA step in one contiguous KiB);
+//   - X rows are 8 pieces of 16 bytes stored XOR-swizzled (piece p of token t
+//     at slot p ^ (t % 8)), so the B fragment reads of 8 consecutive tokens
+//     hit 8 different bank groups.
+// The K order inside a chunk is the blocked layout's: MFMA step s takes, in
+// lane half h, columns 32h + 8s + [0, 8), for both operands.
+template <bool FP16, int D, bool BIAS, bool COMMIT>
+__global__ __launch_bounds__(NTHREADS) void ctx_kv_tiled_kernel(const WriteArgs a, int t_tiles) {
   using E = Elem<FP16>;
   using vec8 = typename E::vec8;
-  constexpr int WAVES_T = 4 / WAVES_N;
-  constexpr int MB = BN / 32 / WAVES_N;  // 32-row blocks per wave
-  constexpr int NB = BT / 32 / WAVES_T;  // 32-token blocks per wave
-  constexpr int CPR = BK / 8;            // 16-byte chunks per operand row slice
-  constexpr int W_CHUNKS = BN * CPR / NTHREADS;
-  constexpr int X_CHUNKS = BT * CPR / NTHREADS;
-  static_assert(MB >= 1 && NB >= 1 && W_CHUNKS >= 1 && X_CHUNKS >= 1, "tile shape");
-  static_assert(BN % D == 0, "a tile holds whole heads");
-
-  constexpr int SW = BN * LDK;
-  constexpr int SX = BT * LDK;
-  constexpr int LDO = BN + 4;  // output tile row: 264 bytes, 8-byte aligned rows
-  constexpr int OPER = 2 * (SW + SX);
-  constexpr int OUT = BT * LDO;
-  __shared__ __align__(16) uint16_t smem[OPER > OUT ? OPER : OUT];
-  uint16_t* sW = smem;
-  uint16_t* sX = smem + 2 * SW;
+  constexpr int BT = 256;
+  constexpr int STAGES = 3;
+  constexpr int MB = 2;                    // 32-row blocks per wave
+  constexpr int NB = 4;                    // 32-token blocks per wave
+  constexpr int SW = BN * BK;              // weight elements per stage (one block)
+  constexpr int SXE = BT * BK;             // X elements per stage
+  constexpr int STAGE = SW + SXE;
+  constexpr int W_PER_THREAD = SW / 8 / NTHREADS;   // 4 direct loads
+  constexpr int X_PER_THREAD = SXE / 8 / NTHREADS;  // 8 direct loads
+  constexpr int LOADS = W_PER_THREAD + X_PER_THREAD;
+  constexpr int LDO = BN + 4;
+  static_assert(STAGES * STAGE >= BT * LDO, "output tile fits in the operand stages");
+  __shared__ __align__(16) uint16_t smem[STAGES * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wave_n = wave / WAVES_T;
-  const int wave_t = wave % WAVES_T;
-
+  const int wave_n = wave >> 1;
+  const int wave_t = wave & 1;
+  const int r32 = lane & 31;
+  const int hh = lane >> 5;
   const int64_t T = a.T;
   const int H = a.H;
-  const int64_t t_tiles = (T + BT - 1) / BT;
-  const int64_t bid = blockIdx.x;
-  const int64_t t_blk = bid % t_tiles;
-  const int64_t n_blk = bid / t_tiles;
-  const int64_t n0 = n_blk * BN;
-  const int64_t t0 = t_blk * BT;
   const int nk = (H + BK - 1) / BK;
 
-  uint4 rw[W_CHUNKS];
-  uint4 rx[X_CHUNKS];
+  // Tile order: groups of 4 row tiles x all token tiles, walked row-fastest,
+  // and each XCD (workgroup b runs on XCD b % 8) takes a contiguous run of
+  // that order, so the ~32 workgroups resident on one XCD share 4 weight
+  // tiles and 8 token tiles through its L2.
+  const int64_t R = (int64_t)a.L * 2 * a.NH * D / BN;
+  const int64_t ntiles = R * t_tiles;
+  const int64_t b = blockIdx.x;
+  const int64_t j = ntiles % 8 == 0 ? (b % 8) * (ntiles / 8) + b / 8 : b;
+  constexpr int64_t G = 4;
+  const int64_t gsz = G * t_tiles;
+  const int64_t g0 = (j / gsz) * G;
+  const int64_t rows_in_group = R - g0 < G ? R - g0 : G;
+  const int64_t jr = j % gsz;
+  const int64_t rt = g0 + jr % rows_in_group;
+  const int64_t tt = jr / rows_in_group;
+  const int64_t n0 = rt * BN;
+  const int64_t t0 = tt * BT;
 
-  auto load = [&](int kt) {
-    const int k0 = kt * BK;
+  const uint16_t* wtile = a.w + rt * nk * 8192;
+  auto issue = [&](int c, int stage) {
+    uint16_t* base = smem + stage * STAGE;
 #pragma unroll
-    for (int i = 0; i < W_CHUNKS; ++i) {
-      const int c = tid + i * NTHREADS;
-      const int row = c / CPR;
-      const int k = k0 + (c % CPR) * 8;
-      rw[i] = ldg16(k < H ? a.w + (n0 + row) * (int64_t)H + k : a.zeros);
+    for (int i = 0; i < W_PER_THREAD; ++i) {
+      const int q0 = i * NTHREADS + wave * 64;  // this wave's first piece
+      const uint16_t* src = c < nk ? wtile + (int64_t)c * 8192 + (q0 + lane) * 8 : a.zeros;
+      ldg16_to_lds(src, base + q0 * 8);
     }
 #pragma unroll
-    for (int i = 0; i < X_CHUNKS; ++i) {
-      const int c = tid + i * NTHREADS;
-      const int row = c / CPR;
-      const int k = k0 + (c % CPR) * 8;
-      const int64_t t = t0 + row < T ? t0 + row : T - 1;  // rows past T are never stored
-      rx[i] = ldg16(k < H ? a.x + t * a.x_stride + k : a.zeros);
-    }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < W_CHUNKS; ++i) {
-      const int c = tid + i * NTHREADS;
-      *reinterpret_cast<uint4*>(sW + buf * SW + (c / CPR) * LDK + (c % CPR) * 8) = rw[i];
-    }
-#pragma unroll
-    for (int i = 0; i < X_CHUNKS; ++i) {
-      const int c = tid + i * NTHREADS;
-      *reinterpret_cast<uint4*>(sX + buf * SX + (c / CPR) * LDK + (c % CPR) * 8) = rx[i];
+    for (int i = 0; i < X_PER_THREAD; ++i) {
+      const int s0 = i * NTHREADS + wave * 64;  // this wave's first LDS slot
+      const int slot = s0 + lane;
+      const int t = slot / 8;
+      const int piece = (slot % 8) ^ (t % 8);
+      const int64_t tok = t0 + t < T ? t0 + t : T - 1;  // rows past T are never stored
+      const int k = c * BK + piece * 8;
+      const uint16_t* src = k < H ? a.x + tok * a.x_stride + k : a.zeros;
+      ldg16_to_lds(src, base + SW + s0 * 8);
     }
   };
 
@@ -260,48 +291,58 @@ __global__ __launch_bounds__(NTHREADS) void ctx_kv_write_kernel(const WriteArgs 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
 
-  load(0);
-  store(0);
-  lds_barrier();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    load(kt + 1);  // past the last slice this reads the zero page
-    const uint16_t* cw = sW + cur * SW;
-    const uint16_t* cx = sX + cur * SX;
+  // Whole turns of the stage ring with no branches (chunks past the end read
+  // the zero page), so the stage index is a compile-time constant.
+  const int nk_ring = (nk + STAGES - 1) / STAGES * STAGES;
+  issue(0, 0);
+  issue(1, 1);
+  for (int c0 = 0; c0 < nk_ring; c0 += STAGES) {
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      // lane l supplies row (l % 32) and the 8 consecutive k at 8 * (l / 32)
-      const int kof = kk * 16 + (lane >> 5) * 8;
-      vec8 af[MB], bfr[NB];
+    for (int s = 0; s < STAGES; ++s) {
+      wait_vmcnt<LOADS>();  // this thread's loads of chunk c0 + s have landed
+      raw_barrier();        // ... and every other thread's; stage (s + 2) % 3 is free
+      issue(c0 + s + 2, (s + 2) % STAGES);
+      const uint16_t* ws = smem + s * STAGE;
+      const uint16_t* xs = ws + SW;
+      // fragments of step kk + 1 are read while the MFMAs of step kk run
+      vec8 af[2][MB], bfr[2][NB];
+      auto read_frags = [&](int kk, vec8(&fa)[MB], vec8(&fb)[NB]) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        af[mb] = *reinterpret_cast<const vec8*>(
-            cw + (wave_n * MB * 32 + mb * 32 + (lane & 31)) * LDK + kof);
+        for (int mb = 0; mb < MB; ++mb)
+          fa[mb] = *reinterpret_cast<const vec8*>(
+              ws + (((wave_n * MB + mb) * 4 + kk) * 64 + lane) * 8);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        bfr[nb] = *reinterpret_cast<const vec8*>(
-            cx + (wave_t * NB * 32 + nb * 32 + (lane & 31)) * LDK + kof);
+        for (int nb = 0; nb < NB; ++nb) {
+          const int t = wave_t * 128 + nb * 32 + r32;
+          const int slot = (4 * hh + kk) ^ (t % 8);
+          fb[nb] = *reinterpret_cast<const vec8*>(xs + (t * 8 + slot) * 8);
+        }
+      };
+      read_frags(0, af[0], bfr[0]);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        if (kk + 1 < BK / 16) read_frags(kk + 1, af[(kk + 1) & 1], bfr[(kk + 1) & 1]);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = E::mfma(af[mb], bfr[nb], acc[mb][nb]);
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            acc[mb][nb] = E::mfma(af[kk & 1][mb], bfr[kk & 1][nb], acc[mb][nb]);
+      }
     }
-    store(cur ^ 1);
-    lds_barrier();
   }
+  wait_vmcnt<0>();  // the two prefetches past the end (zero page) are done
+  raw_barrier();
 
-  // ---- epilogue 1: accumulators (+ bias) -> dtype, into the LDS tile [BT][LDO].
-  // 32x32 accumulator layout: lane l holds column (token) l % 32 and, in
-  // register r, row 8 * (r / 4) + 4 * (l / 32) + r % 4.
+  // accumulators (+ bias) -> dtype, into the LDS tile [BT][LDO]
   uint16_t* sO = smem;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int tok = wave_t * NB * 32 + nb * 32 + (lane & 31);
+      const int tok = wave_t * 128 + nb * 32 + r32;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int row = wave_n * MB * 32 + mb * 32 + 8 * q + 4 * (lane >> 5);
+        const int row = wave_n * 64 + mb * 32 + 8 * q + 4 * hh;
         float v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -316,7 +357,6 @@ __global__ __launch_bounds__(NTHREADS) void ctx_kv_write_kernel(const WriteArgs 
     }
   }
   __syncthreads();
-
   scatter_tile<E, D, BT, COMMIT, LDO>(a, sO, n0, t0, tid);
 }
 
@@ -371,17 +411,15 @@ __global__ __launch_bounds__(NTHREADS) void ctx_kv_stream_kernel(const WriteArgs
   const int64_t n0 = rt * BN;
   const int64_t t0 = sp * BT;
   const int nk = (H + BK - 1) / BK;
-  const uint16_t* wrow = a.w + (n0 + 32 * wave + r32) * (int64_t)H + 32 * hh;
+  // this wave's pieces of block (rt, c): one contiguous KiB per MFMA step
+  const uint16_t* wblk = a.w + rt * nk * 8192 + (wave * 4 * 64 + lane) * 8;
 
   uint4 wq[PF][4];
   uint4 rx[PF][XC];
   auto load_chunk = [&](int c, uint4(&wd)[4], uint4(&xd)[XC]) {
     const int k0 = c * BK;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k = k0 + 32 * hh + 8 * j;
-      wd[j] = ldg16(k < H ? wrow + k0 + 8 * j : a.zeros);
-    }
+    for (int j = 0; j < 4; ++j) wd[j] = ldg16(c < nk ? wblk + (int64_t)c * 8192 + j * 512 : a.zeros);
 #pragma unroll
     for (int i = 0; i < XC; ++i) {
       const int e = tid + i * NTHREADS;
@@ -460,12 +498,13 @@ __global__ __launch_bounds__(NTHREADS) void ctx_kv_stream_kernel(const WriteArgs
 
 template <bool FP16, int D, bool BIAS, bool COMMIT>
 hipError_t launch_tiled(const WriteArgs& a, hipStream_t stream) {
-  constexpr int BT = 128;
+  constexpr int BT = 256;
   const int64_t n_tiles = (int64_t)a.L * 2 * a.NH * D / BN;
-  const int64_t grid = n_tiles * ((a.T + BT - 1) / BT);
-  if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((ctx_kv_write_kernel<FP16, D, BIAS, COMMIT, BT, 2>), dim3((uint32_t)grid),
-                     dim3(NTHREADS), 0, stream, a);
+  const int64_t t_tiles = (a.T + BT - 1) / BT;
+  const int64_t grid = n_tiles * t_tiles;
+  if (grid <= 0 || grid > 0x7FFFFFFF || t_tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((ctx_kv_tiled_kernel<FP16, D, BIAS, COMMIT>), dim3((uint32_t)grid),
+                     dim3(NTHREADS), 0, stream, a, (int)t_tiles);
   return hipGetLastError();
 }
 

@@ -14,7 +14,7 @@ constexpr int kMaxLayers = DSPARK_MAX_LAYERS;
 // arguments so that one launch can address every layer's pool.
 struct WriteArgs {
   const uint16_t* x;        // ctx_hidden [T, H] (row stride x_stride)
-  const uint16_t* w;        // W_stacked [N_tot, H], N_tot = L * 2 * NH * D
+  const uint16_t* w;        // W_stacked in the blocked layout, N_tot = L * 2 * NH * D rows
   const uint16_t* bias;     // [N_tot] or nullptr
   const float* knw;         // [L, D] fp32
   const uint16_t* zeros;    // 16 zero bytes: the source of K-tail lanes past H
@@ -46,6 +46,10 @@ hipError_t launch_ctx_kv_write(const WriteArgs& a, int head_dim, bool is_fp16, b
 
 // Pack helpers.
 hipError_t launch_widen_to_f32(const void* src, int dtype, float* dst, int64_t n,
+                               hipStream_t stream);
+// Rewrites a plain row-major [rows, H] weight (rows % 128 == 0) into the
+// blocked layout the write kernels read.
+hipError_t launch_block_weight(const uint16_t* plain, int64_t rows, int64_t H, uint16_t* blk,
                                hipStream_t stream);
 hipError_t launch_compare_f32(const float* a, const float* b, int64_t n, int* differ,
                               hipStream_t stream);

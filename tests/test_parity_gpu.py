@@ -93,18 +93,32 @@ def test_workload(name, sample):
 
 # ------------------------------------------------------------ structure and invariants
 
+def _unblock(blk, rows, H):
+    """Inverse of the blocked weight layout documented at dspark_pack_buffers:
+    block (rt, c) = 1024 pieces of 8; piece q = (g*4 + s)*64 + l is row
+    128 rt + 32 g + l % 32, columns 64 c + 32 (l // 32) + 8 s + [0, 8)."""
+    nk = -(-H // 64)
+    pieces = blk.reshape(rows // 128, nk, 4, 4, 2, 32, 8)  # rt, c, g, s, half, l%32, e
+    # -> rt, g, l%32, c, half, s, e  = row-major [rows, nk*64]
+    plain = pieces.transpose(0, 2, 5, 1, 4, 3, 6).reshape(rows, nk * 64)
+    assert not plain[:, H:].any()  # padding columns are zero
+    return plain[:, :H]
+
+
 def test_pack_contents():
     """W_stacked is the layers' KV slices in layer order (K rows then V rows),
     the bias is stacked the same way, k_norm is widened to fp32 exactly."""
-    case = W.make_case(T=8, H=64, L=3, NH=1, D=128, dtype="fp16", bias=True, seed=22, slots=16)
+    case = W.make_case(T=8, H=72, L=3, NH=1, D=128, dtype="fp16", bias=True, seed=22, slots=16)
     dc = DeviceCase(case)
     pack = dc.pack()
     info = pack.info()
-    assert info == dict(num_layers=3, hidden=64, kv_size=128, head_dim=128, act_dtype=dk.FP16,
+    assert info == dict(num_layers=3, hidden=72, kv_size=128, head_dim=128, act_dtype=dk.FP16,
                         has_bias=True)
     w_ptr, b_ptr, k_ptr = pack.buffers()
     n_tot = case.L * 2 * case.kv
-    w = device_to_host(w_ptr, n_tot * case.H * 2).view(np.uint16).reshape(n_tot, case.H)
+    nk = -(-case.H // 64)
+    blk = device_to_host(w_ptr, n_tot * nk * 64 * 2).view(np.uint16)
+    w = _unblock(blk, n_tot, case.H)
     b = device_to_host(b_ptr, n_tot * 2).view(np.uint16)
     kn = device_to_host(k_ptr, case.L * case.D * 4).view(np.float32).reshape(case.L, case.D)
     sl = slice(case.q_size, case.q_size + 2 * case.kv)
