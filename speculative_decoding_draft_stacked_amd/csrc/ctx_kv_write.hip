@@ -210,8 +210,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 //   - the chunk's weight block is copied linearly (the blocked layout already
 //     puts each wave's A fragment for one MFMA step in one contiguous KiB);
 //   - X rows are 8 pieces of 16 bytes stored XOR-swizzled (piece p of token t
-//     at slot p ^ (t % 8)), so the B fragment reads of 8 consecutive tokens
-//     hit 8 different bank groups.
+//     at slot p ^ ((t / 2) % 8)). The LDS serves 16 lanes x 16 bytes per
+//     cycle over 64 banks; token t's row starts in bank half t % 2, and the
+//     swizzle spreads 16 consecutive tokens over all 16 bank groups.
 // The K order inside a chunk is the blocked layout's: MFMA step s takes, in
 // lane half h, columns 32h + 8s + [0, 8), for both operands.
 template <bool FP16, int D, bool BIAS, bool COMMIT>
@@ -275,7 +276,7 @@ __global__ __launch_bounds__(NTHREADS) void ctx_kv_tiled_kernel(const WriteArgs 
       const int s0 = i * NTHREADS + wave * 64;  // this wave's first LDS slot
       const int slot = s0 + lane;
       const int t = slot / 8;
-      const int piece = (slot % 8) ^ (t % 8);
+      const int piece = (slot % 8) ^ ((t >> 1) & 7);
       const int64_t tok = t0 + t < T ? t0 + t : T - 1;  // rows past T are never stored
       const int k = c * BK + piece * 8;
       const uint16_t* src = k < H ? a.x + tok * a.x_stride + k : a.zeros;
@@ -314,7 +315,7 @@ __global__ __launch_bounds__(NTHREADS) void ctx_kv_tiled_kernel(const WriteArgs 
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           const int t = wave_t * 128 + nb * 32 + r32;
-          const int slot = (4 * hh + kk) ^ (t % 8);
+          const int slot = (4 * hh + kk) ^ ((t >> 1) & 7);
           fb[nb] = *reinterpret_cast<const vec8*>(xs + (t * 8 + slot) * 8);
         }
       };
