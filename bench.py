@@ -34,6 +34,7 @@ INFINITY_CACHE_BYTES = 256 << 20
 KERNEL_SOURCE = os.path.join(ROOT, "speculative_decoding_draft_stacked_amd", "csrc",
                              "ctx_kv_write.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+COPY_PROBE_BYTES = 1 << 30
 
 
 def log(*a):
@@ -72,6 +73,63 @@ def measured_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
+def _counter_means(csv_dir: str, kernel_substr: str) -> dict:
+    """Mean per-dispatch counter values of the kernels whose name contains
+    `kernel_substr`, from a rocprofv3 --pmc --output-format csv directory."""
+    import collections
+    import csv
+    import glob
+
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    for path in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            if kernel_substr in r["Kernel_Name"]:
+                per[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no dispatch of '{kernel_substr}' in {csv_dir}")
+    names = set(k for d in per.values() for k in d)
+    return {n: sum(d.get(n, 0.0) for d in per.values()) / len(per) for n in names}
+
+
+def record_traffic(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str,
+                   copy_write_dir: str, kernel: str, command: str) -> None:
+    """Store HBM bytes per launch of the write kernel in profiles/traffic.json:
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the kernel, each scaled so
+    that the same counter reads the true bytes of a plain copy of COPY_PROBE_BYTES."""
+    copy_fetch = _counter_means(copy_fetch_dir, "copyBuffer")["FETCH_SIZE"]
+    copy_write = _counter_means(copy_write_dir, "copyBuffer")["WRITE_SIZE"]
+    fetch_scale = COPY_PROBE_BYTES / (copy_fetch * 1024)
+    write_scale = COPY_PROBE_BYTES / (copy_write * 1024)
+    fetch = _counter_means(fetch_dir, kernel)["FETCH_SIZE"]
+    write = _counter_means(write_dir, kernel)["WRITE_SIZE"]
+    rec = {}
+    if os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE))
+    rec[workload] = {
+        "kernel": kernel, "kernel_sha": kernel_source_hash(),
+        "fetch_kib": fetch, "write_kib": write,
+        "fetch_scale": fetch_scale, "write_scale": write_scale,
+        "bytes_per_launch": round(fetch * 1024 * fetch_scale + write * 1024 * write_scale),
+        "command": command,
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    print(json.dumps(rec[workload]))
+
+
+def copy_probe() -> None:
+    """A plain device copy of COPY_PROBE_BYTES, three times (counter calibration)."""
+    import torch
+
+    src = torch.ones(COPY_PROBE_BYTES // 2, dtype=torch.int16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "copies": 3}))
+
+
 def cpu_baseline(case, seconds: float) -> dict:
     """The CPU oracle on the same batch, repeated for about `seconds`."""
     import numpy as np
@@ -104,7 +162,19 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch steps one by one (no graph)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--record-traffic", nargs=5,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR", "KERNEL"),
+                    help="store scaled FETCH_SIZE/WRITE_SIZE of KERNEL for --workload")
+    ap.add_argument("--command", default="", help="command line recorded with --record-traffic")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(args.workload, *args.record_traffic, command=args.command)
+        return 0
+    if args.copy_probe:
+        copy_probe()
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
