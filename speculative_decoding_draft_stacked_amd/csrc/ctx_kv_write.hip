@@ -112,18 +112,17 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
 // each V head, and scatter both into the token's slot of the head's layer pool.
 // Each (token, head) is handled by D/16 lanes; lane j owns elements
 // [8j, 8j+8) of the first half and their rotation partners 8j + D/2 + [0, 8).
-template <typename E, int D, int BT, bool COMMIT, int LDO>
+template <typename E, int D, int BT, bool COMMIT, int LDO, int NT = NTHREADS>
 __device__ __forceinline__ void scatter_tile(const WriteArgs& a, const uint16_t* sO, int64_t n0,
                                              int64_t t0, int tid) {
   const int64_t T = a.T;
   constexpr int TPH = D / 16;  // lanes per (token, head)
   constexpr int HPT = BN / D;  // heads per tile
-  constexpr int ROUNDS = BT * HPT * TPH / NTHREADS;
-  static_assert(ROUNDS * NTHREADS == BT * HPT * TPH, "epilogue work split");
+  constexpr int TASK_LANES = BT * HPT * TPH;
+  static_assert(NT % 64 == 0 && TASK_LANES % TPH == 0, "lane groups stay inside a wave");
   const int two_nh = 2 * a.NH;
 #pragma unroll 1
-  for (int r = 0; r < ROUNDS; ++r) {
-    const int idx = r * NTHREADS + tid;
+  for (int idx = tid; idx < TASK_LANES; idx += NT) {
     const int task = idx / TPH;
     const int j = idx % TPH;
     const int tt = task / HPT;
@@ -361,36 +360,44 @@ __global__ __launch_bounds__(NTHREADS) void ctx_kv_tiled_kernel(const WriteArgs 
   scatter_tile<E, D, BT, COMMIT, LDO>(a, sO, n0, t0, tid);
 }
 
-// Weight-streaming kernel for small T (decode-sized batches). A workgroup owns
-// one 128-row tile of the stacked weight and BT = 32*NB tokens; the host picks
-// the number of token splits so that the whole grid is one round of
-// workgroups. Wave w owns weight rows [32w, 32w+32) of the tile and streams
-// them from HBM straight into a PF-deep register ring (no LDS): for a 64-wide
-// K chunk, lane l holds row l % 32 and the 32 contiguous k at 32*(l / 32).
-// The K order inside a chunk is permuted to match: MFMA step kk takes, in lane
-// half h, k = 32h + 8kk + [0, 8), and the X operand is read from LDS with the
-// same permutation (a sum over k does not depend on its order). X chunks
-// travel through a register ring of the same depth into double-buffered LDS,
-// so every wait on an X load also only waits for weight loads of the same
-// chunk (loads complete in issue order).
-template <bool FP16, int D, bool BIAS, bool COMMIT, int NB, int PF>
-__global__ __launch_bounds__(NTHREADS) void ctx_kv_stream_kernel(const WriteArgs a, int splits) {
+// Weight-streaming kernel for small T (decode-sized batches). A workgroup
+// owns one 128-row tile of the stacked weight and BT = 32*NB tokens; the host
+// picks the number of token splits so that the whole grid is one round of
+// workgroups. Eight waves, two per SIMD: wave (w, par) owns weight rows
+// [32w, 32w+32) of the tile and the K chunks of parity par (K is split
+// inside the workgroup; the two halves are added through LDS at the end), so
+// each SIMD interleaves two instruction streams.
+//   - Weight: streamed from HBM straight into a per-wave register ring (the
+//     blocked layout gives each MFMA A fragment as one contiguous KiB).
+//   - X: direct-to-LDS loads into an 8-stage ring, rows XOR-swizzled for
+//     conflict-free 16-lane B fragment reads; no register staging.
+//   - Chunks are consumed in groups of two (one per parity) with one barrier
+//     per group; loads run LOOK groups ahead, so each wait covers only the
+//     group about to be used.
+template <bool FP16, int D, bool BIAS, bool COMMIT, int NB>
+__global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, int splits) {
   using E = Elem<FP16>;
   using vec8 = typename E::vec8;
-  static_assert(PF % 2 == 0, "the LDS double buffer is indexed by ring slot parity");
+  constexpr int NT = 512;
   constexpr int BT = 32 * NB;
-  constexpr int XC = BT * (BK / 8) / NTHREADS;  // 16-byte X pieces per thread per chunk
-  static_assert(XC * NTHREADS == BT * (BK / 8), "X chunk split");
-  constexpr int LDX = BK + 8;
-  constexpr int SXS = BT * LDX;
-  constexpr int LDO = BN + 4;
-  constexpr int OPER = 2 * SXS;
-  constexpr int OUT = BT * LDO;
-  __shared__ __align__(16) uint16_t smem[OPER > OUT ? OPER : OUT];
+  constexpr int LOOK = 3;             // groups issued ahead of the one being computed
+  constexpr int SLOTS = LOOK + 1;     // per-wave weight ring slots (one chunk per group)
+  constexpr int XSTAGES = 2 * SLOTS;  // X stages (one chunk each)
+  constexpr int SXE = BT * BK;        // X stage elements
+  constexpr int XPW = SXE / 8 / 256;  // X direct loads per thread per chunk (= NB)
+  constexpr int LOADS = 4 + XPW;      // per thread per group
+  constexpr int LDO = BN + 4;         // rounded output tile row (elements)
+  constexpr int RS = BN + 4;          // fp32 partial row (floats): 528 bytes, conflict-free
+  constexpr int XBYTES = XSTAGES * SXE * 2;
+  constexpr int EBYTES = BT * RS * 4 + BT * LDO * 2;
+  static_assert(XPW * 256 * 8 == SXE, "X chunk split");
+  __shared__ __align__(16) uint16_t smem[(XBYTES > EBYTES ? XBYTES : EBYTES) / 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int w = wave & 3;     // 32-row group
+  const int par = wave >> 2;  // K-chunk parity
   const int r32 = lane & 31;
   const int hh = lane >> 5;
   const int64_t T = a.T;
@@ -412,28 +419,41 @@ __global__ __launch_bounds__(NTHREADS) void ctx_kv_stream_kernel(const WriteArgs
   const int64_t n0 = rt * BN;
   const int64_t t0 = sp * BT;
   const int nk = (H + BK - 1) / BK;
-  // this wave's pieces of block (rt, c): one contiguous KiB per MFMA step
-  const uint16_t* wblk = a.w + rt * nk * 8192 + (wave * 4 * 64 + lane) * 8;
+  const int ng = (nk + 1) / 2;
+  const int ng_ring = (ng + SLOTS - 1) / SLOTS * SLOTS;
 
-  uint4 wq[PF][4];
-  uint4 rx[PF][XC];
-  auto load_chunk = [&](int c, uint4(&wd)[4], uint4(&xd)[XC]) {
-    const int k0 = c * BK;
+  // this wave's pieces of weight block (rt, c): one contiguous KiB per MFMA step
+  const uint16_t* wblk = a.w + rt * nk * 8192 + (w * 4 * 64 + lane) * 8;
+  // X direct loads: instruction i of wave (w, par) fills LDS slots
+  // [256 i + 64 w, +64) of its chunk's stage; slot s holds piece
+  // (s % 8) ^ ((t / 2) % 8) of token t = s / 8. Per-lane source offsets are
+  // the same for every chunk.
+  int64_t xoff[XPW];
+  int xcol[XPW];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) wd[j] = ldg16(c < nk ? wblk + (int64_t)c * 8192 + j * 512 : a.zeros);
+  for (int i = 0; i < XPW; ++i) {
+    const int slot = i * 256 + w * 64 + lane;
+    const int t = slot / 8;
+    const int piece = (slot % 8) ^ ((t >> 1) & 7);
+    const int64_t tok = t0 + t < T ? t0 + t : T - 1;  // rows past T are never stored
+    xoff[i] = tok * a.x_stride + piece * 8;
+    xcol[i] = piece * 8;
+  }
+
+  uint4 wq[SLOTS][4];
+  auto issue = [&](int g, uint4(&wd)[4]) {
+    const int c = 2 * g + par;
+    const bool live = c < nk;  // chunks past the end read the zero page
+    const uint16_t* wsrc = live ? wblk + (int64_t)c * 8192 : a.zeros;
+    const int wstep = live ? 512 : 0;
 #pragma unroll
-    for (int i = 0; i < XC; ++i) {
-      const int e = tid + i * NTHREADS;
-      const int64_t t = t0 + e / 8 < T ? t0 + e / 8 : T - 1;  // rows past T are never stored
-      const int k = k0 + (e % 8) * 8;
-      xd[i] = ldg16(k < H ? a.x + t * a.x_stride + k : a.zeros);
-    }
-  };
-  auto stage_x = [&](int buf, const uint4(&xd)[XC]) {
+    for (int kk = 0; kk < 4; ++kk) wd[kk] = ldg16(wsrc + kk * wstep);
+    uint16_t* stage = smem + ((c % XSTAGES) * SXE);
+    const int kbase = c * BK;
 #pragma unroll
-    for (int i = 0; i < XC; ++i) {
-      const int e = tid + i * NTHREADS;
-      *reinterpret_cast<uint4*>(smem + buf * SXS + (e / 8) * LDX + (e % 8) * 8) = xd[i];
+    for (int i = 0; i < XPW; ++i) {
+      const bool ok = live && kbase + xcol[i] < H;
+      ldg16_to_lds(ok ? a.x + xoff[i] + kbase : a.zeros, stage + (i * 256 + w * 64) * 8);
     }
   };
 
@@ -443,58 +463,69 @@ __global__ __launch_bounds__(NTHREADS) void ctx_kv_stream_kernel(const WriteArgs
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[tb][r] = 0.0f;
 
-  // The loop runs a whole number of ring turns with no branches, so the
-  // compiler's load counters stay exact; chunks past the end read the zero
-  // page and add nothing.
-  const int nk_ring = (nk + PF - 1) / PF * PF;
 #pragma unroll
-  for (int s = 0; s < PF; ++s) load_chunk(s, wq[s], rx[s]);
-  stage_x(0, rx[0]);
-  lds_barrier();
-
-  for (int c0 = 0; c0 < nk_ring; c0 += PF) {
+  for (int g = 0; g < LOOK; ++g) issue(g, wq[g]);
+  for (int g0 = 0; g0 < ng_ring; g0 += SLOTS) {
 #pragma unroll
-    for (int s = 0; s < PF; ++s) {
-      const int c = c0 + s;
-      const uint16_t* xs = smem + (s & 1) * SXS;  // chunk c sits in buffer c & 1 == s & 1
+    for (int u = 0; u < SLOTS; ++u) {
+      wait_vmcnt<(LOOK - 1) * LOADS>();  // this thread's loads of group g0 + u landed
+      raw_barrier();                     // ... and everyone's; group g0 + u - 1 is free
+      issue(g0 + u + LOOK, wq[(u + LOOK) % SLOTS]);
+      const uint16_t* xs = smem + ((2 * u + par) % XSTAGES) * SXE;
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
-        const vec8 av = __builtin_bit_cast(vec8, wq[s][kk]);
+        const vec8 av = __builtin_bit_cast(vec8, wq[u][kk]);
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb) {
-          const vec8 bv =
-              *reinterpret_cast<const vec8*>(xs + (tb * 32 + r32) * LDX + 32 * hh + 8 * kk);
+          const int t = tb * 32 + r32;
+          const int slot = (4 * hh + kk) ^ ((t >> 1) & 7);
+          const vec8 bv = *reinterpret_cast<const vec8*>(xs + (t * 8 + slot) * 8);
           acc[tb] = E::mfma(av, bv, acc[tb]);
         }
       }
-      stage_x((s + 1) & 1, rx[(s + 1) % PF]);
-      load_chunk(c + PF, wq[s], rx[s]);
-      lds_barrier();
     }
   }
+  wait_vmcnt<0>();  // prefetches past the end (zero page) are done
+  raw_barrier();
 
-  // accumulators (+ bias) -> dtype, into the LDS tile [BT][LDO]
-  uint16_t* sO = smem;
+  // add the two K halves, (+ bias), round to the dtype into the LDS tile [BT][LDO]
+  float* red = reinterpret_cast<float*>(smem);
+  uint16_t* sO = smem + BT * RS * 2;
+  if (par == 1) {
 #pragma unroll
-  for (int tb = 0; tb < NB; ++tb) {
-    const int tok = tb * 32 + r32;
+    for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int row = 32 * wave + 8 * q + 4 * hh;
-      float v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[i] = acc[tb][4 * q + i];
-        if (BIAS) v[i] += E::to_f(a.bias[n0 + row + i]);
+      for (int q = 0; q < 4; ++q) {
+        const int tok = tb * 32 + r32;
+        const int row = 32 * w + 8 * q + 4 * hh;
+        *reinterpret_cast<float4*>(red + tok * RS + row) =
+            make_float4(acc[tb][4 * q], acc[tb][4 * q + 1], acc[tb][4 * q + 2], acc[tb][4 * q + 3]);
       }
-      uint2 packed;
-      packed.x = E::from_f(v[0]) | (E::from_f(v[1]) << 16);
-      packed.y = E::from_f(v[2]) | (E::from_f(v[3]) << 16);
-      *reinterpret_cast<uint2*>(sO + tok * LDO + row) = packed;
+  }
+  __syncthreads();
+  if (par == 0) {
+#pragma unroll
+    for (int tb = 0; tb < NB; ++tb) {
+      const int tok = tb * 32 + r32;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = 32 * w + 8 * q + 4 * hh;
+        const float4 o = *reinterpret_cast<const float4*>(red + tok * RS + row);
+        float v[4] = {acc[tb][4 * q] + o.x, acc[tb][4 * q + 1] + o.y, acc[tb][4 * q + 2] + o.z,
+                      acc[tb][4 * q + 3] + o.w};
+        if (BIAS) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] += E::to_f(a.bias[n0 + row + i]);
+        }
+        uint2 packed;
+        packed.x = E::from_f(v[0]) | (E::from_f(v[1]) << 16);
+        packed.y = E::from_f(v[2]) | (E::from_f(v[3]) << 16);
+        *reinterpret_cast<uint2*>(sO + tok * LDO + row) = packed;
+      }
     }
   }
   __syncthreads();
-  scatter_tile<E, D, BT, COMMIT, LDO>(a, sO, n0, t0, tid);
+  scatter_tile<E, D, BT, COMMIT, LDO, NT>(a, sO, n0, t0, tid);
 }
 
 template <bool FP16, int D, bool BIAS, bool COMMIT>
@@ -511,9 +542,8 @@ hipError_t launch_tiled(const WriteArgs& a, hipStream_t stream) {
 
 template <bool FP16, int D, bool BIAS, bool COMMIT, int NB>
 hipError_t launch_stream_nb(const WriteArgs& a, int64_t row_tiles, int splits, hipStream_t stream) {
-  constexpr int PF = NB == 1 ? 8 : (NB == 4 ? 4 : 6);
-  hipLaunchKernelGGL((ctx_kv_stream_kernel<FP16, D, BIAS, COMMIT, NB, PF>),
-                     dim3((uint32_t)(row_tiles * splits)), dim3(NTHREADS), 0, stream, a, splits);
+  hipLaunchKernelGGL((ctx_kv_stream_kernel<FP16, D, BIAS, COMMIT, NB>),
+                     dim3((uint32_t)(row_tiles * splits)), dim3(512), 0, stream, a, splits);
   return hipGetLastError();
 }
 
