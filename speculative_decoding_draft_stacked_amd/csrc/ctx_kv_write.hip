@@ -112,12 +112,12 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
 // each V head, and scatter both into the token's slot of the head's layer pool.
 // Each (token, head) is handled by D/16 lanes; lane j owns elements
 // [8j, 8j+8) of the first half and their rotation partners 8j + D/2 + [0, 8).
-template <typename E, int D, int BT, bool COMMIT, int LDO, int NT = NTHREADS>
+template <typename E, int D, int BT, bool COMMIT, int LDO, int NT = NTHREADS, int ROWS = BN>
 __device__ __forceinline__ void scatter_tile(const WriteArgs& a, const uint16_t* sO, int64_t n0,
                                              int64_t t0, int tid) {
   const int64_t T = a.T;
-  constexpr int TPH = D / 16;  // lanes per (token, head)
-  constexpr int HPT = BN / D;  // heads per tile
+  constexpr int TPH = D / 16;    // lanes per (token, head)
+  constexpr int HPT = ROWS / D;  // heads per tile
   constexpr int TASK_LANES = BT * HPT * TPH;
   static_assert(NT % 64 == 0 && TASK_LANES % TPH == 0, "lane groups stay inside a wave");
   const int two_nh = 2 * a.NH;
@@ -134,6 +134,7 @@ __device__ __forceinline__ void scatter_tile(const WriteArgs& a, const uint16_t*
     if (COMMIT) valid = valid && (t % a.W) < a.commit[t / a.W];
     if (!valid) continue;
     const int64_t g = (n0 + hd * D) / D;  // global head: layer-major, K heads then V heads
+    if (g >= (int64_t)a.L * two_nh) continue;  // rows past the stacked weight (last tile)
     const int layer = (int)(g / two_nh);
     const int jj = (int)(g % two_nh);
     const bool is_k = jj < a.NH;
@@ -201,85 +202,102 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// LDS-tiled kernel for large T. A workgroup owns one 128-row weight tile and
-// BT = 256 tokens; its 4 waves form a 2 x 2 grid of 64-row x 128-token wave
-// tiles (2 x 4 MFMA blocks each). Every 64-wide K chunk is brought into one of
-// three LDS stages by direct-to-LDS loads, two chunks ahead of the MFMAs, with
-// no register staging:
-//   - the chunk's weight block is copied linearly (the blocked layout already
-//     puts each wave's A fragment for one MFMA step in one contiguous KiB);
+// LDS-tiled kernel for large T. A workgroup owns a 256-row x 256-token tile
+// (two 128-row weight tiles; the second may lie past the stacked weight when
+// the number of 128-row tiles is odd). Eight waves, two per SIMD, form a 4 x 2
+// grid of 64-row x 128-token wave tiles (2 x 4 MFMA blocks each). Every
+// 64-wide K chunk is brought into one of two 64 KiB LDS stages by direct-to-LDS
+// loads, one chunk ahead of the MFMAs, with no register staging:
+//   - the two weight blocks are copied linearly (the blocked layout puts each
+//     wave's A fragment for one MFMA step in one contiguous KiB);
 //   - X rows are 8 pieces of 16 bytes stored XOR-swizzled (piece p of token t
 //     at slot p ^ ((t / 2) % 8)). The LDS serves 16 lanes x 16 bytes per
 //     cycle over 64 banks; token t's row starts in bank half t % 2, and the
 //     swizzle spreads 16 consecutive tokens over all 16 bank groups.
-// The K order inside a chunk is the blocked layout's: MFMA step s takes, in
-// lane half h, columns 32h + 8s + [0, 8), for both operands.
+// The tile is twice as tall as the weight tile so that each K chunk costs half
+// the line requests per MFMA of a 128-row tile. The K order inside a chunk is
+// the blocked layout's: MFMA step s takes, in lane half h, columns
+// 32h + 8s + [0, 8), for both operands.
 template <bool FP16, int D, bool BIAS, bool COMMIT>
-__global__ __launch_bounds__(NTHREADS) void ctx_kv_tiled_kernel(const WriteArgs a, int t_tiles) {
+__global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, int t_tiles) {
   using E = Elem<FP16>;
   using vec8 = typename E::vec8;
+  constexpr int NT = 512;
+  constexpr int ROWS = 2 * BN;              // 256 weight rows per workgroup
   constexpr int BT = 256;
-  constexpr int STAGES = 3;
-  constexpr int MB = 2;                    // 32-row blocks per wave
-  constexpr int NB = 4;                    // 32-token blocks per wave
-  constexpr int SW = BN * BK;              // weight elements per stage (one block)
-  constexpr int SXE = BT * BK;             // X elements per stage
+  constexpr int MB = 2;                     // 32-row blocks per wave
+  constexpr int NB = 4;                     // 32-token blocks per wave
+  constexpr int SW = 2 * BN * BK;           // weight elements per stage (two blocks)
+  constexpr int SXE = BT * BK;              // X elements per stage
   constexpr int STAGE = SW + SXE;
-  constexpr int W_PER_THREAD = SW / 8 / NTHREADS;   // 4 direct loads
-  constexpr int X_PER_THREAD = SXE / 8 / NTHREADS;  // 8 direct loads
-  constexpr int LOADS = W_PER_THREAD + X_PER_THREAD;
-  constexpr int LDO = BN + 4;
-  static_assert(STAGES * STAGE >= BT * LDO, "output tile fits in the operand stages");
-  __shared__ __align__(16) uint16_t smem[STAGES * STAGE];
+  constexpr int W_PER_THREAD = SW / 8 / NT;   // 4 direct loads
+  constexpr int X_PER_THREAD = SXE / 8 / NT;  // 4 direct loads
+  constexpr int LDO = ROWS + 4;
+  constexpr int SMEM = (2 * STAGE > BT * LDO ? 2 * STAGE : BT * LDO);
+  __shared__ __align__(16) uint16_t smem[SMEM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wave_n = wave >> 1;
-  const int wave_t = wave & 1;
+  const int wave_n = wave >> 1;  // 64-row group
+  const int wave_t = wave & 1;   // 128-token half
   const int r32 = lane & 31;
   const int hh = lane >> 5;
   const int64_t T = a.T;
   const int H = a.H;
   const int nk = (H + BK - 1) / BK;
 
-  // Tile order: groups of 4 row tiles x all token tiles, walked row-fastest,
+  // Tile order: groups of 4 row pairs x all token tiles, walked row-fastest,
   // and each XCD (workgroup b runs on XCD b % 8) takes a contiguous run of
-  // that order, so the ~32 workgroups resident on one XCD share 4 weight
-  // tiles and 8 token tiles through its L2.
-  const int64_t R = (int64_t)a.L * 2 * a.NH * D / BN;
-  const int64_t ntiles = R * t_tiles;
+  // that order, so the workgroups resident on one XCD share weight and token
+  // tiles through its L2.
+  const int64_t R = (int64_t)a.L * 2 * a.NH * D / BN;  // 128-row weight tiles
+  const int64_t RP = (R + 1) / 2;                       // 256-row tiles
+  const int64_t ntiles = RP * t_tiles;
   const int64_t b = blockIdx.x;
   const int64_t j = ntiles % 8 == 0 ? (b % 8) * (ntiles / 8) + b / 8 : b;
   constexpr int64_t G = 4;
   const int64_t gsz = G * t_tiles;
   const int64_t g0 = (j / gsz) * G;
-  const int64_t rows_in_group = R - g0 < G ? R - g0 : G;
+  const int64_t rows_in_group = RP - g0 < G ? RP - g0 : G;
   const int64_t jr = j % gsz;
-  const int64_t rt = g0 + jr % rows_in_group;
+  const int64_t rp = g0 + jr % rows_in_group;
   const int64_t tt = jr / rows_in_group;
-  const int64_t n0 = rt * BN;
+  const int64_t n0 = rp * ROWS;
   const int64_t t0 = tt * BT;
 
-  const uint16_t* wtile = a.w + rt * nk * 8192;
+  // Per-lane sources that do not change with the chunk.
+  const uint16_t* wsrc[W_PER_THREAD];
+#pragma unroll
+  for (int i = 0; i < W_PER_THREAD; ++i) {
+    const int q = i * NT + tid;     // piece of the stage's two blocks
+    const int64_t rt = 2 * rp + q / 1024;
+    wsrc[i] = rt < R ? a.w + rt * nk * 8192 + (q % 1024) * 8 : nullptr;
+  }
+  int64_t xoff[X_PER_THREAD];
+  int xcol[X_PER_THREAD];
+#pragma unroll
+  for (int i = 0; i < X_PER_THREAD; ++i) {
+    const int slot = i * NT + tid;
+    const int t = slot / 8;
+    const int piece = (slot % 8) ^ ((t >> 1) & 7);
+    const int64_t tok = t0 + t < T ? t0 + t : T - 1;  // rows past T are never stored
+    xoff[i] = tok * a.x_stride + piece * 8;
+    xcol[i] = piece * 8;
+  }
   auto issue = [&](int c, int stage) {
     uint16_t* base = smem + stage * STAGE;
+    const bool live = c < nk;  // chunks past the end read the zero page
 #pragma unroll
     for (int i = 0; i < W_PER_THREAD; ++i) {
-      const int q0 = i * NTHREADS + wave * 64;  // this wave's first piece
-      const uint16_t* src = c < nk ? wtile + (int64_t)c * 8192 + (q0 + lane) * 8 : a.zeros;
-      ldg16_to_lds(src, base + q0 * 8);
+      const uint16_t* src = live && wsrc[i] ? wsrc[i] + (int64_t)c * 8192 : a.zeros;
+      ldg16_to_lds(src, base + (i * NT + wave * 64) * 8);
     }
 #pragma unroll
     for (int i = 0; i < X_PER_THREAD; ++i) {
-      const int s0 = i * NTHREADS + wave * 64;  // this wave's first LDS slot
-      const int slot = s0 + lane;
-      const int t = slot / 8;
-      const int piece = (slot % 8) ^ ((t >> 1) & 7);
-      const int64_t tok = t0 + t < T ? t0 + t : T - 1;  // rows past T are never stored
-      const int k = c * BK + piece * 8;
-      const uint16_t* src = k < H ? a.x + tok * a.x_stride + k : a.zeros;
-      ldg16_to_lds(src, base + SW + s0 * 8);
+      const int k = c * BK + xcol[i];
+      const uint16_t* src = live && k < H ? a.x + xoff[i] + c * BK : a.zeros;
+      ldg16_to_lds(src, base + SW + (i * NT + wave * 64) * 8);
     }
   };
 
@@ -291,26 +309,29 @@ __global__ __launch_bounds__(NTHREADS) void ctx_kv_tiled_kernel(const WriteArgs 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
 
-  // Whole turns of the stage ring with no branches (chunks past the end read
-  // the zero page), so the stage index is a compile-time constant.
-  const int nk_ring = (nk + STAGES - 1) / STAGES * STAGES;
+  // Whole turns of the two-stage ring with no branches (chunks past the end
+  // read the zero page), so the stage index is a compile-time constant.
+  const int nk_ring = (nk + 1) / 2 * 2;
   issue(0, 0);
-  issue(1, 1);
-  for (int c0 = 0; c0 < nk_ring; c0 += STAGES) {
+  for (int c0 = 0; c0 < nk_ring; c0 += 2) {
 #pragma unroll
-    for (int s = 0; s < STAGES; ++s) {
-      wait_vmcnt<LOADS>();  // this thread's loads of chunk c0 + s have landed
-      raw_barrier();        // ... and every other thread's; stage (s + 2) % 3 is free
-      issue(c0 + s + 2, (s + 2) % STAGES);
+    for (int s = 0; s < 2; ++s) {
+      wait_vmcnt<0>();  // this thread's loads of chunk c0 + s have landed
+      raw_barrier();    // ... and every other thread's; the other stage is free
+      issue(c0 + s + 1, s ^ 1);
       const uint16_t* ws = smem + s * STAGE;
       const uint16_t* xs = ws + SW;
       // fragments of step kk + 1 are read while the MFMAs of step kk run
       vec8 af[2][MB], bfr[2][NB];
       auto read_frags = [&](int kk, vec8(&fa)[MB], vec8(&fb)[NB]) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < MB; ++mb) {
+          const int r = wave_n * 64 + mb * 32;   // first row of the 32-row block
+          const int blk = r / BN;                // which of the two weight blocks
+          const int grp = (r % BN) / 32;         // 32-row group inside the block
           fa[mb] = *reinterpret_cast<const vec8*>(
-              ws + (((wave_n * MB + mb) * 4 + kk) * 64 + lane) * 8);
+              ws + blk * (BN * BK) + ((grp * 4 + kk) * 64 + lane) * 8);
+        }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           const int t = wave_t * 128 + nb * 32 + r32;
@@ -330,10 +351,11 @@ __global__ __launch_bounds__(NTHREADS) void ctx_kv_tiled_kernel(const WriteArgs 
       }
     }
   }
-  wait_vmcnt<0>();  // the two prefetches past the end (zero page) are done
+  wait_vmcnt<0>();  // the prefetch past the end (zero page) is done
   raw_barrier();
 
   // accumulators (+ bias) -> dtype, into the LDS tile [BT][LDO]
+  const int64_t n_tot = R * BN;
   uint16_t* sO = smem;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -347,7 +369,7 @@ __global__ __launch_bounds__(NTHREADS) void ctx_kv_tiled_kernel(const WriteArgs 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           v[i] = acc[mb][nb][4 * q + i];
-          if (BIAS) v[i] += E::to_f(a.bias[n0 + row + i]);
+          if (BIAS && n0 + row + i < n_tot) v[i] += E::to_f(a.bias[n0 + row + i]);
         }
         uint2 packed;
         packed.x = E::from_f(v[0]) | (E::from_f(v[1]) << 16);
@@ -357,7 +379,7 @@ __global__ __launch_bounds__(NTHREADS) void ctx_kv_tiled_kernel(const WriteArgs 
     }
   }
   __syncthreads();
-  scatter_tile<E, D, BT, COMMIT, LDO>(a, sO, n0, t0, tid);
+  scatter_tile<E, D, BT, COMMIT, LDO, NT, ROWS>(a, sO, n0, t0, tid);
 }
 
 // Weight-streaming kernel for small T (decode-sized batches). A workgroup
@@ -531,12 +553,12 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
 template <bool FP16, int D, bool BIAS, bool COMMIT>
 hipError_t launch_tiled(const WriteArgs& a, hipStream_t stream) {
   constexpr int BT = 256;
-  const int64_t n_tiles = (int64_t)a.L * 2 * a.NH * D / BN;
+  const int64_t r_tiles = (int64_t)a.L * 2 * a.NH * D / BN;
   const int64_t t_tiles = (a.T + BT - 1) / BT;
-  const int64_t grid = n_tiles * t_tiles;
+  const int64_t grid = (r_tiles + 1) / 2 * t_tiles;
   if (grid <= 0 || grid > 0x7FFFFFFF || t_tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((ctx_kv_tiled_kernel<FP16, D, BIAS, COMMIT>), dim3((uint32_t)grid),
-                     dim3(NTHREADS), 0, stream, a, (int)t_tiles);
+  hipLaunchKernelGGL((ctx_kv_tiled_kernel<FP16, D, BIAS, COMMIT>), dim3((uint32_t)grid), dim3(512),
+                     0, stream, a, (int)t_tiles);
   return hipGetLastError();
 }
 

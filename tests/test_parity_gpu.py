@@ -58,6 +58,12 @@ SMALL = {
     "T32": dict(T=32, H=128, L=2, NH=2, D=64, slots=64),
     "T513_theta1e6": dict(T=513, H=64, L=1, NH=1, D=128, slots=1024, theta=1e6, P=32768),
     "T1000_multi_layer": dict(T=1000, H=128, L=5, NH=2, D=64, slots=2048, row_width=8),
+    # large-T path: an odd number of 128-row weight tiles (the last 256-row
+    # workgroup tile is half past the stacked weight), K tail H % 64 = 8
+    "tiled_odd_row_tiles": dict(T=11000, H=72, L=3, NH=1, D=64, slots=12000),
+    # large-T path: ragged token tail, K tail, commit window 10 with holes
+    "tiled_commit_holes": dict(T=8300, H=136, L=2, NH=1, D=128, row_width=10,
+                               commit_range=(0, 12), neg_loc_frac=0.05, slots=9000),
 }
 
 
