@@ -202,22 +202,33 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// s_waitcnt vmcnt(N) lgkmcnt(0): before a ring barrier, this wave's loads of
+// the next stage have landed and its own LDS reads of the stage about to be
+// refilled have completed (the compiler may issue them late, right before the
+// barrier), so no direct-to-LDS write issued after the barrier can overtake one.
+template <int N>
+__device__ __forceinline__ void wait_ring() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
 // LDS-tiled kernel for large T. A workgroup owns a 256-row x 256-token tile
 // (two 128-row weight tiles; the second may lie past the stacked weight when
 // the number of 128-row tiles is odd). Eight waves, two per SIMD, form a 4 x 2
-// grid of 64-row x 128-token wave tiles (2 x 4 MFMA blocks each). Every
-// 64-wide K chunk is brought into one of two 64 KiB LDS stages by direct-to-LDS
-// loads, one chunk ahead of the MFMAs, with no register staging:
-//   - the two weight blocks are copied linearly (the blocked layout puts each
-//     wave's A fragment for one MFMA step in one contiguous KiB);
-//   - X rows are 8 pieces of 16 bytes stored XOR-swizzled (piece p of token t
-//     at slot p ^ ((t / 2) % 8)). The LDS serves 16 lanes x 16 bytes per
-//     cycle over 64 banks; token t's row starts in bank half t % 2, and the
-//     swizzle spreads 16 consecutive tokens over all 16 bank groups.
-// The tile is twice as tall as the weight tile so that each K chunk costs half
-// the line requests per MFMA of a 128-row tile. The K order inside a chunk is
-// the blocked layout's: MFMA step s takes, in lane half h, columns
-// 32h + 8s + [0, 8), for both operands.
+// grid of 64-row x 128-token wave tiles (2 x 4 MFMA blocks each). The K loop
+// runs over 32-wide sub-chunks (two MFMA steps) through a four-stage LDS ring
+// of 32 KiB stages filled by direct-to-LDS loads three sub-chunks ahead, so
+// the memory pipe never drains between sub-chunks:
+//   - weight: the blocked layout holds, per 64-column chunk, each 32-row group's
+//     A fragment for one MFMA step as one contiguous KiB; a sub-chunk copies
+//     the two steps it needs linearly;
+//   - X: a sub-chunk needs 4 of the 8 16-byte pieces of each token's 64-column
+//     slice (MFMA step s, lane half h takes columns 32h + 8s + [0, 8)); they
+//     sit in a 64-byte LDS row, logical piece p of token t at slot
+//     p ^ ((t / 4) % 4). The LDS serves 16 lanes x 16 bytes per cycle over 64
+//     banks; 16 consecutive tokens then cover all 16 bank groups.
+// The tile is twice as tall as the weight tile so that each K step costs half
+// the line requests per MFMA of a 128-row tile.
 template <bool FP16, int D, bool BIAS, bool COMMIT>
 __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, int t_tiles) {
   using E = Elem<FP16>;
@@ -227,13 +238,17 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
   constexpr int BT = 256;
   constexpr int MB = 2;                     // 32-row blocks per wave
   constexpr int NB = 4;                     // 32-token blocks per wave
-  constexpr int SW = 2 * BN * BK;           // weight elements per stage (two blocks)
-  constexpr int SXE = BT * BK;              // X elements per stage
+  constexpr int SK = 32;                    // K per sub-chunk
+  constexpr int STAGES = 4;
+  constexpr int LOOK = STAGES - 1;          // sub-chunks in flight ahead of the MFMAs
+  constexpr int SW = ROWS * SK;             // weight elements per stage
+  constexpr int SXE = BT * SK;              // X elements per stage
   constexpr int STAGE = SW + SXE;
-  constexpr int W_PER_THREAD = SW / 8 / NT;   // 4 direct loads
-  constexpr int X_PER_THREAD = SXE / 8 / NT;  // 4 direct loads
+  constexpr int W_PER_THREAD = SW / 8 / NT;   // 2 direct loads
+  constexpr int X_PER_THREAD = SXE / 8 / NT;  // 2 direct loads
+  constexpr int LOADS = W_PER_THREAD + X_PER_THREAD;
   constexpr int LDO = ROWS + 4;
-  constexpr int SMEM = (2 * STAGE > BT * LDO ? 2 * STAGE : BT * LDO);
+  constexpr int SMEM = (STAGES * STAGE > BT * LDO ? STAGES * STAGE : BT * LDO);
   __shared__ __align__(16) uint16_t smem[SMEM];
 
   const int tid = threadIdx.x;
@@ -266,37 +281,43 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
   const int64_t n0 = rp * ROWS;
   const int64_t t0 = tt * BT;
 
-  // Per-lane sources that do not change with the chunk.
+  // Per-lane sources for the first half of chunk 0. Stage piece q of the
+  // weight is (block q / 512, group g, step s' of the half, lane l).
   const uint16_t* wsrc[W_PER_THREAD];
 #pragma unroll
   for (int i = 0; i < W_PER_THREAD; ++i) {
-    const int q = i * NT + tid;     // piece of the stage's two blocks
-    const int64_t rt = 2 * rp + q / 1024;
-    wsrc[i] = rt < R ? a.w + rt * nk * 8192 + (q % 1024) * 8 : nullptr;
+    const int q = i * NT + tid;
+    const int64_t rt = 2 * rp + q / 512;
+    const int g = (q % 512) / 128, sp = (q % 128) / 64, l = q % 64;
+    wsrc[i] = rt < R ? a.w + rt * nk * 8192 + ((g * 4 + sp) * 64 + l) * 8 : nullptr;
   }
   int64_t xoff[X_PER_THREAD];
   int xcol[X_PER_THREAD];
 #pragma unroll
   for (int i = 0; i < X_PER_THREAD; ++i) {
     const int slot = i * NT + tid;
-    const int t = slot / 8;
-    const int piece = (slot % 8) ^ ((t >> 1) & 7);
+    const int t = slot / 4;
+    const int lp = (slot % 4) ^ ((t >> 2) & 3);   // logical piece held by this slot
+    const int col = 8 * ((lp / 2) * 4 + lp % 2);  // its column in the first half
     const int64_t tok = t0 + t < T ? t0 + t : T - 1;  // rows past T are never stored
-    xoff[i] = tok * a.x_stride + piece * 8;
-    xcol[i] = piece * 8;
+    xoff[i] = tok * a.x_stride + col;
+    xcol[i] = col;
   }
-  auto issue = [&](int c, int stage) {
+  // sub-chunk sc = half sc % 2 of 64-column chunk sc / 2; the second half
+  // takes MFMA steps 2 and 3, i.e. pieces 2, 3, 6, 7
+  auto issue = [&](int sc, int stage) {
     uint16_t* base = smem + stage * STAGE;
-    const bool live = c < nk;  // chunks past the end read the zero page
+    const int c = sc >> 1, h = sc & 1;
+    const bool live = c < nk;  // sub-chunks past the end read the zero page
 #pragma unroll
     for (int i = 0; i < W_PER_THREAD; ++i) {
-      const uint16_t* src = live && wsrc[i] ? wsrc[i] + (int64_t)c * 8192 : a.zeros;
+      const uint16_t* src = live && wsrc[i] ? wsrc[i] + (int64_t)c * 8192 + h * 1024 : a.zeros;
       ldg16_to_lds(src, base + (i * NT + wave * 64) * 8);
     }
 #pragma unroll
     for (int i = 0; i < X_PER_THREAD; ++i) {
-      const int k = c * BK + xcol[i];
-      const uint16_t* src = live && k < H ? a.x + xoff[i] + c * BK : a.zeros;
+      const int k = c * BK + 16 * h + xcol[i];
+      const uint16_t* src = live && k < H ? a.x + xoff[i] + c * BK + 16 * h : a.zeros;
       ldg16_to_lds(src, base + SW + (i * NT + wave * 64) * 8);
     }
   };
@@ -309,49 +330,50 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
 
-  // Whole turns of the two-stage ring with no branches (chunks past the end
-  // read the zero page), so the stage index is a compile-time constant.
-  const int nk_ring = (nk + 1) / 2 * 2;
-  issue(0, 0);
-  for (int c0 = 0; c0 < nk_ring; c0 += 2) {
+  // Whole turns of the ring with no branches (sub-chunks past the end read
+  // the zero page), so stage indices are compile-time constants and every
+  // wait count is exact.
+  const int nsub = 2 * nk;
+  const int nsub_ring = (nsub + STAGES - 1) / STAGES * STAGES;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      wait_vmcnt<0>();  // this thread's loads of chunk c0 + s have landed
-      raw_barrier();    // ... and every other thread's; the other stage is free
-      issue(c0 + s + 1, s ^ 1);
-      const uint16_t* ws = smem + s * STAGE;
+  for (int u = 0; u < LOOK; ++u) issue(u, u);
+  for (int c0 = 0; c0 < nsub_ring; c0 += STAGES) {
+#pragma unroll
+    for (int u = 0; u < STAGES; ++u) {
+      wait_ring<(LOOK - 1) * LOADS>();  // this thread's loads of sub-chunk c0 + u landed
+      raw_barrier();                     // ... and everyone's; stage (u - 1) % STAGES is free
+      issue(c0 + u + LOOK, (u + LOOK) % STAGES);
+      const uint16_t* ws = smem + u * STAGE;
       const uint16_t* xs = ws + SW;
-      // fragments of step kk + 1 are read while the MFMAs of step kk run
       vec8 af[2][MB], bfr[2][NB];
-      auto read_frags = [&](int kk, vec8(&fa)[MB], vec8(&fb)[NB]) {
+      auto read_frags = [&](int sp, vec8(&fa)[MB], vec8(&fb)[NB]) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          const int r = wave_n * 64 + mb * 32;   // first row of the 32-row block
-          const int blk = r / BN;                // which of the two weight blocks
-          const int grp = (r % BN) / 32;         // 32-row group inside the block
-          fa[mb] = *reinterpret_cast<const vec8*>(
-              ws + blk * (BN * BK) + ((grp * 4 + kk) * 64 + lane) * 8);
+          const int r = wave_n * 64 + mb * 32;  // first row of the 32-row block
+          const int blk = r / BN;               // which of the two weight blocks
+          const int grp = (r % BN) / 32;        // 32-row group inside the block
+          fa[mb] = *reinterpret_cast<const vec8*>(ws + blk * (BN * SK) +
+                                                  ((grp * 2 + sp) * 64 + lane) * 8);
         }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           const int t = wave_t * 128 + nb * 32 + r32;
-          const int slot = (4 * hh + kk) ^ ((t >> 1) & 7);
-          fb[nb] = *reinterpret_cast<const vec8*>(xs + (t * 8 + slot) * 8);
+          const int slot = (2 * hh + sp) ^ ((t >> 2) & 3);
+          fb[nb] = *reinterpret_cast<const vec8*>(xs + (t * 4 + slot) * 8);
         }
       };
       read_frags(0, af[0], bfr[0]);
+      read_frags(1, af[1], bfr[1]);
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        if (kk + 1 < BK / 16) read_frags(kk + 1, af[(kk + 1) & 1], bfr[(kk + 1) & 1]);
+      for (int sp = 0; sp < 2; ++sp)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb)
-            acc[mb][nb] = E::mfma(af[kk & 1][mb], bfr[kk & 1][nb], acc[mb][nb]);
-      }
+            acc[mb][nb] = E::mfma(af[sp][mb], bfr[sp][nb], acc[mb][nb]);
     }
   }
-  wait_vmcnt<0>();  // the prefetch past the end (zero page) is done
+  wait_ring<0>();  // the prefetches past the end (zero page) are done, LDS reads too
   raw_barrier();
 
   // accumulators (+ bias) -> dtype, into the LDS tile [BT][LDO]
@@ -490,7 +512,7 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
   for (int g0 = 0; g0 < ng_ring; g0 += SLOTS) {
 #pragma unroll
     for (int u = 0; u < SLOTS; ++u) {
-      wait_vmcnt<(LOOK - 1) * LOADS>();  // this thread's loads of group g0 + u landed
+      wait_ring<(LOOK - 1) * LOADS>();  // this thread's loads of group g0 + u landed
       raw_barrier();                     // ... and everyone's; group g0 + u - 1 is free
       issue(g0 + u + LOOK, wq[(u + LOOK) % SLOTS]);
       const uint16_t* xs = smem + ((2 * u + par) % XSTAGES) * SXE;
@@ -507,7 +529,7 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
       }
     }
   }
-  wait_vmcnt<0>();  // prefetches past the end (zero page) are done
+  wait_ring<0>();  // prefetches past the end (zero page) are done, LDS reads too
   raw_barrier();
 
   // add the two K halves, (+ bias), round to the dtype into the LDS tile [BT][LDO]

@@ -58,6 +58,17 @@ SMALL = {
     "T32": dict(T=32, H=128, L=2, NH=2, D=64, slots=64),
     "T513_theta1e6": dict(T=513, H=64, L=1, NH=1, D=128, slots=1024, theta=1e6, P=32768),
     "T1000_multi_layer": dict(T=1000, H=128, L=5, NH=2, D=64, slots=2048, row_width=8),
+    # wider hidden with a K tail H % 64 = 40, 9 weight tiles, commit window 7
+    # with holes
+    "wide_h_odd_tiles_ktail": dict(T=77, H=1000, L=3, NH=3, D=64, row_width=7,
+                                   commit_range=(0, 9), neg_loc_frac=0.1, slots=300),
+    # 33 K chunks with a tail of 8, 8 weight tiles
+    "wide_h_eight_tiles": dict(T=200, H=2056, L=2, NH=2, D=128, slots=256),
+    # fp16 + bias over 12 K chunks, ragged token tail
+    "wide_h_fp16_bias": dict(T=300, H=768, L=1, NH=2, D=64, dtype="fp16", bias=True,
+                             slots=512),
+    # one row against a 4096-wide hidden
+    "single_row_wide_h": dict(T=1, H=4096, L=2, NH=1, D=128, slots=8),
     # large-T path: an odd number of 128-row weight tiles (the last 256-row
     # workgroup tile is half past the stacked weight), K tail H % 64 = 8
     "tiled_odd_row_tiles": dict(T=11000, H=72, L=3, NH=1, D=64, slots=12000),
