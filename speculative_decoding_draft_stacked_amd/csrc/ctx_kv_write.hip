@@ -229,20 +229,22 @@ __device__ __forceinline__ void wait_ring() {
 //     banks; 16 consecutive tokens then cover all 16 bank groups.
 // The tile is twice as tall as the weight tile so that each K step costs half
 // the line requests per MFMA of a 128-row tile.
-template <bool FP16, int D, bool BIAS, bool COMMIT>
+template <bool FP16, int D, bool BIAS, bool COMMIT, int BT>
 __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, int t_tiles) {
   using E = Elem<FP16>;
   using vec8 = typename E::vec8;
   constexpr int NT = 512;
   constexpr int ROWS = 2 * BN;              // 256 weight rows per workgroup
-  constexpr int BT = 256;
   constexpr int MB = 2;                     // 32-row blocks per wave
-  constexpr int NB = 4;                     // 32-token blocks per wave
+  constexpr int NB = BT / 64;               // 32-token blocks per wave
+  static_assert(BT % 64 == 0 && BT <= 256, "token tile");
   constexpr int SK = 32;                    // K per sub-chunk
   constexpr int STAGES = 4;
   constexpr int LOOK = STAGES - 1;          // sub-chunks in flight ahead of the MFMAs
   constexpr int SW = ROWS * SK;             // weight elements per stage
-  constexpr int SXE = BT * SK;              // X elements per stage
+  // X stage slots: whole rounds of 512 pieces; slots of tokens >= BT read
+  // the zero page so that every thread issues the same loads
+  constexpr int SXE = (BT * SK / 8 + NT - 1) / NT * NT * 8;
   constexpr int STAGE = SW + SXE;
   constexpr int W_PER_THREAD = SW / 8 / NT;   // 2 direct loads
   constexpr int X_PER_THREAD = SXE / 8 / NT;  // 2 direct loads
@@ -301,7 +303,7 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
     const int col = 8 * ((lp / 2) * 4 + lp % 2);  // its column in the first half
     const int64_t tok = t0 + t < T ? t0 + t : T - 1;  // rows past T are never stored
     xoff[i] = tok * a.x_stride + col;
-    xcol[i] = col;
+    xcol[i] = t < BT ? col : H;  // slots past the tile read the zero page
   }
   // sub-chunk sc = half sc % 2 of 64-column chunk sc / 2; the second half
   // takes MFMA steps 2 and 3, i.e. pieces 2, 3, 6, 7
@@ -357,7 +359,7 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
         }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          const int t = wave_t * 128 + nb * 32 + r32;
+          const int t = wave_t * (BT / 2) + nb * 32 + r32;
           const int slot = (2 * hh + sp) ^ ((t >> 2) & 3);
           fb[nb] = *reinterpret_cast<const vec8*>(xs + (t * 4 + slot) * 8);
         }
@@ -383,7 +385,7 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
   for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int tok = wave_t * 128 + nb * 32 + r32;
+      const int tok = wave_t * (BT / 2) + nb * 32 + r32;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int row = wave_n * 64 + mb * 32 + 8 * q + 4 * hh;
@@ -572,16 +574,36 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
   scatter_tile<E, D, BT, COMMIT, LDO, NT>(a, sO, n0, t0, tid);
 }
 
-template <bool FP16, int D, bool BIAS, bool COMMIT>
-hipError_t launch_tiled(const WriteArgs& a, hipStream_t stream) {
-  constexpr int BT = 256;
-  const int64_t r_tiles = (int64_t)a.L * 2 * a.NH * D / BN;
-  const int64_t t_tiles = (a.T + BT - 1) / BT;
-  const int64_t grid = (r_tiles + 1) / 2 * t_tiles;
-  if (grid <= 0 || grid > 0x7FFFFFFF || t_tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((ctx_kv_tiled_kernel<FP16, D, BIAS, COMMIT>), dim3((uint32_t)grid), dim3(512),
-                     0, stream, a, (int)t_tiles);
+template <bool FP16, int D, bool BIAS, bool COMMIT, int BT>
+hipError_t launch_tiled_bt(const WriteArgs& a, int64_t grid, int64_t t_tiles, hipStream_t stream) {
+  hipLaunchKernelGGL((ctx_kv_tiled_kernel<FP16, D, BIAS, COMMIT, BT>), dim3((uint32_t)grid),
+                     dim3(512), 0, stream, a, (int)t_tiles);
   return hipGetLastError();
+}
+
+// Token tile of the large-T kernel: the one with the least (rounds of
+// workgroups over the device) x (tokens per tile), i.e. the shortest
+// critical path when every tile of a size costs about the same; ties go to
+// the larger tile, which needs fewer line requests per MFMA.
+template <bool FP16, int D, bool BIAS, bool COMMIT>
+hipError_t launch_tiled(const WriteArgs& a, int num_cus, hipStream_t stream) {
+  const int64_t r_tiles = (int64_t)a.L * 2 * a.NH * D / BN;
+  const int64_t rp = (r_tiles + 1) / 2;
+  int best_bt = 256;
+  int64_t best_cost = -1;
+  for (int bt : {256, 192, 128}) {
+    const int64_t grid = rp * ((a.T + bt - 1) / bt);
+    const int64_t cost = (grid + num_cus - 1) / num_cus * bt;
+    if (best_cost < 0 || cost < best_cost) best_cost = cost, best_bt = bt;
+  }
+  const int64_t t_tiles = (a.T + best_bt - 1) / best_bt;
+  const int64_t grid = rp * t_tiles;
+  if (grid <= 0 || grid > 0x7FFFFFFF || t_tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  switch (best_bt) {
+    case 256: return launch_tiled_bt<FP16, D, BIAS, COMMIT, 256>(a, grid, t_tiles, stream);
+    case 192: return launch_tiled_bt<FP16, D, BIAS, COMMIT, 192>(a, grid, t_tiles, stream);
+    default: return launch_tiled_bt<FP16, D, BIAS, COMMIT, 128>(a, grid, t_tiles, stream);
+  }
 }
 
 template <bool FP16, int D, bool BIAS, bool COMMIT, int NB>
@@ -598,7 +620,7 @@ hipError_t launch_by_rows(const WriteArgs& a, int num_cus, hipStream_t stream) {
   const int64_t row_tiles = (int64_t)a.L * 2 * a.NH * D / BN;
   const int64_t blocks = (a.T + 31) / 32;
   const int64_t cap = row_tiles >= num_cus ? 1 : num_cus / row_tiles;
-  if (blocks > 4 * cap) return launch_tiled<FP16, D, BIAS, COMMIT>(a, stream);
+  if (blocks > 4 * cap) return launch_tiled<FP16, D, BIAS, COMMIT>(a, num_cus, stream);
   int64_t splits = blocks < cap ? blocks : cap;
   const int64_t nb = (blocks + splits - 1) / splits;
   splits = (blocks + nb - 1) / nb;

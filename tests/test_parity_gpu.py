@@ -69,12 +69,20 @@ SMALL = {
                              slots=512),
     # one row against a 4096-wide hidden
     "single_row_wide_h": dict(T=1, H=4096, L=2, NH=1, D=128, slots=8),
-    # large-T path: an odd number of 128-row weight tiles (the last 256-row
+    # Large-T path. The token tile (256, 192 or 128) is picked from the grid it
+    # gives on the device (256 compute units on MI355X); the comments name the
+    # tile each case gets there.
+    # 128-token tiles: an odd number of 128-row weight tiles (the last 256-row
     # workgroup tile is half past the stacked weight), K tail H % 64 = 8
     "tiled_odd_row_tiles": dict(T=11000, H=72, L=3, NH=1, D=64, slots=12000),
-    # large-T path: ragged token tail, K tail, commit window 10 with holes
+    # 128-token tiles: ragged token tail, K tail, commit window 10 with holes
     "tiled_commit_holes": dict(T=8300, H=136, L=2, NH=1, D=128, row_width=10,
                                commit_range=(0, 12), neg_loc_frac=0.05, slots=9000),
+    # 192-token tiles (a ragged tail of 32 tokens), odd weight-tile count
+    "tiled_t192_ragged": dict(T=20000, H=72, L=3, NH=1, D=64, slots=20500),
+    # 256-token tiles (tail of 178), K tail 8, commit window 10 with holes
+    "tiled_t256_commit": dict(T=25010, H=136, L=2, NH=1, D=128, row_width=10,
+                              commit_range=(0, 12), neg_loc_frac=0.05, slots=25100),
 }
 
 
