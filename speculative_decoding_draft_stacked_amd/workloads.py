@@ -222,3 +222,93 @@ def sentinel_pools(case: Case) -> tuple:
     ks = [np.full(shape, SENTINEL, dtype=np.uint16) for _ in range(case.L)]
     vs = [np.full(shape, SENTINEL, dtype=np.uint16) for _ in range(case.L)]
     return ks, vs
+
+
+# ---------------------------------------------------------------------------
+# Inputs of the in-place table QK-RMSNorm + neox RoPE on a fused QKV tensor
+# (sglang PR #31847, key source snippets: ``table_qk_norm_rope_``). A row of the
+# tensor is [Q heads | K heads | V heads | padding up to the row stride].
+
+
+@dataclasses.dataclass
+class QkCase:
+    """One synthetic instance of the in-place QK norm + rotation (host arrays)."""
+
+    name: str
+    dtype: str  # "bf16" | "fp16"
+    T: int
+    NHQ: int
+    NHK: int
+    D: int
+    row_stride: int  # elements per row, >= (NHQ + 2 NHK) * D
+    eps: float
+    theta: float
+    P: int
+    weight_dtype: str  # dtype of the norm weights: the activation dtype or "fp32"
+    qkv: np.ndarray  # uint16 [T, row_stride]
+    q_w: np.ndarray  # [D] uint16 patterns, or float32 when weight_dtype == "fp32"
+    k_w: np.ndarray
+    table: np.ndarray  # float32 [P, D]
+    positions: np.ndarray  # int64 [T]
+
+
+def make_qk_case(
+    *,
+    name: str = "qk_case",
+    T: int,
+    NHQ: int,
+    NHK: int,
+    D: int,
+    dtype: str = BF16,
+    row_pad: int = 0,
+    weight_fp32: bool = False,
+    theta: float = 1e4,
+    P: int = 4096,
+    eps: float = 1e-6,
+    seed: int = 0,
+    positions_mode: str = "uniform",
+) -> QkCase:
+    """Draw one case. Order: head values, per-head scales, q_w, k_w, positions,
+    padding. Head values are N(0, 1) times a per-(token, head) scale e^N(0, 0.5),
+    so that head RMS values differ; V and padding columns are drawn too (they
+    must come back unchanged)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    width = (NHQ + 2 * NHK) * D
+    vals = rng.standard_normal((T, NHQ + 2 * NHK, D))
+    scale = np.exp(rng.standard_normal((T, NHQ + 2 * NHK, 1)) * 0.5)
+    qkv = np.empty((T, width + row_pad), dtype=np.uint16)
+    qkv[:, :width] = to_bits((vals * scale).reshape(T, width), dtype)
+    weight_dtype = "fp32" if weight_fp32 else dtype
+    def weight():
+        w = 1.0 + rng.standard_normal(D) * 0.1
+        return w.astype(np.float32) if weight_fp32 else to_bits(w, dtype)
+    q_w = weight()
+    k_w = weight()
+    if positions_mode == "uniform":
+        positions = rng.integers(0, P, size=T, dtype=np.int64)
+    elif positions_mode == "arange":
+        positions = np.arange(T, dtype=np.int64)
+    else:
+        raise ValueError(positions_mode)
+    if row_pad:
+        qkv[:, width:] = to_bits(rng.standard_normal((T, row_pad)), dtype)
+    return QkCase(name=name, dtype=dtype, T=T, NHQ=NHQ, NHK=NHK, D=D, row_stride=width + row_pad,
+                  eps=eps, theta=theta, P=P, weight_dtype=weight_dtype, qkv=qkv, q_w=q_w,
+                  k_w=k_w, table=rope_table(P, D, theta), positions=positions)
+
+
+# Workloads of the QK op: a Qwen3-8B-like draft layer (32 query heads, 8 KV
+# heads of 128), on a decode block of 32 requests x 8 tokens and on an 8k
+# prompt.
+QK_WORKLOADS = {
+    "qk_decode": dict(T=256, NHQ=32, NHK=8, D=128, dtype=BF16, theta=1e6, P=32768),
+    "qk_prefill_8k": dict(T=8192, NHQ=32, NHK=8, D=128, dtype=BF16, theta=1e6, P=32768,
+                          positions_mode="arange"),
+}
+QK_WORKLOAD_ORDER = ["qk_decode", "qk_prefill_8k"]
+
+
+def qk_workload(name: str) -> QkCase:
+    """The named QK workload with its fixed seed (2000 + its 1-based index)."""
+    seed = 2000 + QK_WORKLOAD_ORDER.index(name) + 1
+    return make_qk_case(name=name, seed=seed, **QK_WORKLOADS[name])
