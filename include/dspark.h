@@ -169,6 +169,43 @@ int dspark_ctx_kv_write(const dspark_ctx_kv_pack* pack, const void* ctx_hidden,
                         int64_t num_requests, const dspark_pool_desc* pools,
                         int32_t num_pools, void* stream, int32_t* fallback_reason);
 
+/* In-place table QK RMSNorm + neox RoPE on a fused QKV tensor (sglang PR
+ * #31847, key source snippets: table_qk_norm_rope_ and
+ * _table_qk_norm_rope_kernel in dflash_utils.py). No pack is involved.
+ *   qkv: device [num_tokens, row_stride] in act_dtype (bf16 or fp16), 16-byte
+ *     aligned, row_stride a multiple of 8 and >= (num_q_heads + num_k_heads) *
+ *     head_dim. A row is [num_q_heads query heads | num_k_heads key heads |
+ *     anything else], each head head_dim (64 or 128) wide: query head h and key
+ *     head j start at columns h * head_dim and (num_q_heads + j) * head_dim.
+ *   positions: device int64 [num_tokens].
+ *   q_norm_weight, k_norm_weight: device [head_dim], 16-byte aligned, in
+ *     act_dtype or fp32 (norm_weight_dtype).
+ *   cos_sin: device fp32 [rope_max_pos, head_dim], row p = cos half | sin half,
+ *     16-byte aligned.
+ *   range_errors: device counter or NULL; see below.
+ * For every token and every query and key head, the head is replaced by
+ * round(round(x * inv * w) rotated), inv = 1 / sqrt(mean(x^2) + eps) in fp32, w
+ * the query or key norm weight, the neox rotation over the pairs (i, i +
+ * head_dim/2) with the cos/sin of the token's position; each rounding is
+ * round-to-nearest-even into act_dtype. Every other column is left untouched.
+ * A token whose position is outside [0, rope_max_pos) is left untouched and, if
+ * range_errors is not NULL, counted there (atomically added, never cleared).
+ * num_tokens == 0 returns DSPARK_OK with nothing enqueued. Enqueued on `stream`;
+ * allocates nothing and does not synchronise.
+ * Returns DSPARK_OK; DSPARK_FALLBACK with *fallback_reason (may be NULL) =
+ * DSPARK_FB_DTYPE (act_dtype not bf16/fp16, or a weight dtype other than
+ * act_dtype/fp32) or DSPARK_FB_SHAPE (head_dim not 64 or 128); DSPARK_E_INVALID
+ * (negative sizes, non-positive head counts, short or unaligned row stride,
+ * NULL or misaligned pointers with num_tokens > 0, rope_max_pos <= 0, eps
+ * negative or not finite); DSPARK_E_DEVICE. */
+int dspark_table_qk_norm_rope(void* qkv, int64_t num_tokens, int64_t row_stride,
+                              const int64_t* positions, int32_t num_q_heads, int32_t num_k_heads,
+                              int32_t head_dim, int32_t act_dtype, const void* q_norm_weight,
+                              const void* k_norm_weight, int32_t norm_weight_dtype, double eps,
+                              const float* cos_sin, int64_t rope_max_pos,
+                              unsigned long long* range_errors, void* stream,
+                              int32_t* fallback_reason);
+
 /* Reads and clears the pack's count of rows skipped for an out-of-range
  * position or slot. Synchronises `stream`. Returns DSPARK_OK or an error. */
 int dspark_pack_range_errors(const dspark_ctx_kv_pack* pack, void* stream, int64_t* count);

@@ -31,7 +31,7 @@ FALLBACK_REASONS = {
 EXPORTS = [
     "dspark_check_eligibility", "dspark_pack_ctx_kv", "dspark_ctx_kv_write",
     "dspark_pack_range_errors", "dspark_pack_info", "dspark_pack_buffers", "dspark_pack_free",
-    "dspark_status_str", "dspark_fallback_str",
+    "dspark_status_str", "dspark_fallback_str", "dspark_table_qk_norm_rope",
 ]
 
 
@@ -100,6 +100,8 @@ def lib() -> ctypes.CDLL:
         L.dspark_pack_info.argtypes = [vp, p_i32, p_i64, p_i64, p_i64, p_i32, p_i32]
         L.dspark_pack_buffers.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                           ctypes.POINTER(vp)]
+        L.dspark_table_qk_norm_rope.argtypes = [vp, i64, i64, vp, i32, i32, i32, i32, vp, vp,
+                                                i32, ctypes.c_double, vp, i64, vp, vp, p_i32]
         L.dspark_pack_free.argtypes = [vp]
         L.dspark_pack_free.restype = None
         L.dspark_status_str.argtypes = [ctypes.c_int]
@@ -107,7 +109,8 @@ def lib() -> ctypes.CDLL:
         L.dspark_fallback_str.argtypes = [ctypes.c_int]
         L.dspark_fallback_str.restype = ctypes.c_char_p
         for name in ("dspark_check_eligibility", "dspark_pack_ctx_kv", "dspark_ctx_kv_write",
-                     "dspark_pack_range_errors", "dspark_pack_info", "dspark_pack_buffers"):
+                     "dspark_pack_range_errors", "dspark_pack_info", "dspark_pack_buffers",
+                     "dspark_table_qk_norm_rope"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -278,4 +281,41 @@ def ctx_kv_write(pack: Pack, ctx_hidden, positions, locs, pools: Sequence[PoolDe
     if st == FALLBACK:
         return False
     _raise_for(st, "dspark_ctx_kv_write")
+    return True
+
+
+def table_qk_norm_rope_raw(qkv: int, num_tokens: int, row_stride: int, positions: int,
+                           num_q_heads: int, num_k_heads: int, head_dim: int, act_dtype: int,
+                           q_norm_weight: int, k_norm_weight: int, norm_weight_dtype: int,
+                           eps: float, cos_sin: int, rope_max_pos: int,
+                           range_errors: Optional[int], stream) -> tuple:
+    """dspark_table_qk_norm_rope on raw device pointers; returns (status, reason)."""
+    reason = ctypes.c_int32(0)
+    st = lib().dspark_table_qk_norm_rope(qkv, num_tokens, row_stride, positions, num_q_heads,
+                                         num_k_heads, head_dim, act_dtype, q_norm_weight,
+                                         k_norm_weight, norm_weight_dtype, eps, cos_sin,
+                                         rope_max_pos, range_errors, _stream(stream),
+                                         ctypes.byref(reason))
+    return st, reason.value
+
+
+def table_qk_norm_rope(qkv, positions, q_norm_weight, k_norm_weight, cos_sin_cache,
+                       num_q_heads: int, num_k_heads: int, head_dim: int, eps: float,
+                       range_errors=None, stream=None) -> bool:
+    """Enqueue the in-place QK norm + rotation on ``qkv`` [T, row_stride]. True
+    when enqueued, False on fallback (nothing changed); ValueError on misuse.
+    ``range_errors`` is an optional int64 device tensor of one element that
+    counts tokens skipped for a position outside the table."""
+    if qkv.dim() != 2 or qkv.stride(1) != 1:
+        raise ValueError("qkv must be [T, row_stride] with unit column stride")
+    st, reason = table_qk_norm_rope_raw(
+        qkv.data_ptr(), qkv.shape[0], qkv.stride(0), positions.data_ptr(), num_q_heads,
+        num_k_heads, head_dim, _dtype_code(qkv), q_norm_weight.data_ptr(),
+        k_norm_weight.data_ptr(),
+        _dtype_code(q_norm_weight) if _dtype_code(q_norm_weight) == _dtype_code(k_norm_weight)
+        else QUANTIZED, eps, cos_sin_cache.data_ptr(), cos_sin_cache.shape[0],
+        None if range_errors is None else range_errors.data_ptr(), stream)
+    if st == FALLBACK:
+        return False
+    _raise_for(st, "dspark_table_qk_norm_rope")
     return True

@@ -249,6 +249,52 @@ int dspark_ctx_kv_write(const dspark_ctx_kv_pack* p, const void* ctx_hidden, int
   return e == hipSuccess ? DSPARK_OK : DSPARK_E_DEVICE;
 }
 
+int dspark_table_qk_norm_rope(void* qkv, int64_t num_tokens, int64_t row_stride,
+                              const int64_t* positions, int32_t num_q_heads, int32_t num_k_heads,
+                              int32_t head_dim, int32_t act_dtype, const void* q_norm_weight,
+                              const void* k_norm_weight, int32_t norm_weight_dtype, double eps,
+                              const float* cos_sin, int64_t rope_max_pos,
+                              unsigned long long* range_errors, void* stream_ptr,
+                              int32_t* fallback_reason) {
+  set_reason(fallback_reason, DSPARK_FB_NONE);
+  if (num_tokens < 0 || num_q_heads <= 0 || num_k_heads <= 0 || head_dim <= 0)
+    return DSPARK_E_INVALID;
+  if (act_dtype != DSPARK_BF16 && act_dtype != DSPARK_FP16)
+    return fallback(fallback_reason, DSPARK_FB_DTYPE);
+  if (norm_weight_dtype != act_dtype && norm_weight_dtype != DSPARK_FP32)
+    return fallback(fallback_reason, DSPARK_FB_DTYPE);
+  if (head_dim != 64 && head_dim != 128) return fallback(fallback_reason, DSPARK_FB_SHAPE);
+  const int64_t heads = (int64_t)num_q_heads + num_k_heads;
+  if (row_stride < heads * head_dim || row_stride % 8 != 0) return DSPARK_E_INVALID;
+  if (!(eps >= 0.0) || eps > 3.0e38) return DSPARK_E_INVALID;
+  if (rope_max_pos <= 0) return DSPARK_E_INVALID;
+  if (num_tokens == 0) return DSPARK_OK;
+  if (!qkv || !positions || !q_norm_weight || !k_norm_weight || !cos_sin) return DSPARK_E_INVALID;
+  const uintptr_t walign = 16;  // 8 weight entries (fp32: 2 x 16 bytes) per vector load
+  if (reinterpret_cast<uintptr_t>(qkv) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(q_norm_weight) % walign != 0 ||
+      reinterpret_cast<uintptr_t>(k_norm_weight) % walign != 0 ||
+      reinterpret_cast<uintptr_t>(cos_sin) % 16 != 0)
+    return DSPARK_E_INVALID;
+  dspark::QkArgs a = {};
+  a.qkv = static_cast<uint16_t*>(qkv);
+  a.pos = positions;
+  a.qw = q_norm_weight;
+  a.kw = k_norm_weight;
+  a.table = cos_sin;
+  a.err = range_errors;
+  a.T = num_tokens;
+  a.row_stride = row_stride;
+  a.P = rope_max_pos;
+  a.NHQ = num_q_heads;
+  a.NHT = (int32_t)heads;
+  a.eps = (float)eps;
+  const hipError_t e = dspark::launch_qk_norm_rope(a, head_dim, act_dtype == DSPARK_FP16,
+                                                   norm_weight_dtype == DSPARK_FP32,
+                                                   static_cast<hipStream_t>(stream_ptr));
+  return e == hipSuccess ? DSPARK_OK : DSPARK_E_DEVICE;
+}
+
 int dspark_pack_range_errors(const dspark_ctx_kv_pack* p, void* stream_ptr, int64_t* count) {
   if (!p || !count) return DSPARK_E_INVALID;
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);

@@ -38,6 +38,27 @@ struct WriteArgs {
   int64_t slots[kMaxLayers];
 };
 
+// Arguments of the in-place table QK norm + rotation.
+struct QkArgs {
+  uint16_t* qkv;            // [T, row_stride]: NHQ query heads, NHK key heads, ...
+  const int64_t* pos;       // [T]
+  const void* qw;           // [D] query norm weight (dtype patterns or fp32)
+  const void* kw;           // [D] key norm weight
+  const float* table;       // [P, D] fp32: cos half | sin half
+  unsigned long long* err;  // tokens skipped for a position outside the table, or nullptr
+  int64_t T;
+  int64_t row_stride;
+  int64_t P;
+  int32_t NHQ;
+  int32_t NHT;              // NHQ + NHK
+  float eps;
+};
+
+// Launches the in-place QK norm + rotation for `a` on `stream` (head_dim 64
+// or 128, validated by the caller). Returns the launch status.
+hipError_t launch_qk_norm_rope(const QkArgs& a, int head_dim, bool is_fp16, bool weight_fp32,
+                               hipStream_t stream);
+
 // Launches the fused GEMM + norm + rotation + scatter for `a` on `stream`.
 // `num_cus` (compute units of the device) sizes the small-T grid. Shapes have
 // been validated by the caller. Returns the launch status.

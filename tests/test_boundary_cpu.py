@@ -142,3 +142,42 @@ def test_invalid_arguments():
     assert lib.dspark_pack_ctx_kv(arr, 2, 256, dk.BF16, None, ctypes.byref(out),
                                   ctypes.byref(reason)) == dk.FALLBACK
     assert out.value is None and reason.value == 4
+
+
+# ------------------------------------------------ in-place table QK norm + rotation
+
+def _qk(T=5, stride=512, D=128, act=dk.BF16, wdt=None, eps=1e-6, P=10, nhq=2, nhk=1):
+    """Call with NULL device pointers: only host-side checks may run."""
+    r = ctypes.c_int32(-7)
+    st = dk.lib().dspark_table_qk_norm_rope(None, T, stride, None, nhq, nhk, D, act, None, None,
+                                             act if wdt is None else wdt, eps, None, P, None,
+                                             None, ctypes.byref(r))
+    return st, r.value
+
+
+def test_qk_empty_call_is_ok_and_enqueues_nothing():
+    assert _qk(T=0) == (dk.OK, 0)
+
+
+@pytest.mark.parametrize("kw,reason", [
+    (dict(D=96), 6), (dict(D=256), 6),                          # SHAPE
+    (dict(act=dk.FP32), 7), (dict(act=dk.QUANTIZED), 7),       # DTYPE
+    (dict(act=dk.BF16, wdt=dk.FP16), 7), (dict(act=dk.FP16, wdt=dk.BF16), 7),
+])
+def test_qk_fallbacks(kw, reason):
+    assert _qk(**kw) == (dk.FALLBACK, reason)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=-1), dict(nhq=0), dict(nhk=-1), dict(stride=3 * 128 - 8), dict(stride=3 * 128 + 4),
+    dict(eps=-1e-6), dict(eps=float("nan")), dict(eps=float("inf")), dict(P=0),
+    dict(),  # NULL pointers with tokens to process
+])
+def test_qk_invalid_arguments(kw):
+    assert _qk(**kw)[0] == dk.E_INVALID
+
+
+def test_qk_weight_dtype_may_be_fp32():
+    # passes the dtype checks and stops at the NULL pointers
+    assert _qk(wdt=dk.FP32) == (dk.E_INVALID, 0)
+    assert _qk(act=dk.FP16, wdt=dk.FP32) == (dk.E_INVALID, 0)
