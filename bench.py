@@ -3,7 +3,9 @@
 
 One step = one dspark_ctx_kv_write over one batch of the workload (GEMM + K
 RMSNorm + neox RoPE + scatter into every layer's pool), inputs resident in HBM.
-Prints ONE JSON line on stdout; progress goes to stderr.
+Prints ONE JSON line on stdout; progress goes to stderr. The workloads
+qk_decode and qk_prefill_8k time the in-place table QK-RMSNorm + neox RoPE
+(dspark_table_qk_norm_rope) instead, one call per step.
 
 Timing: W warmup steps, then exactly K steps, each bracketed by a device
 synchronisation. The steps are captured into a HIP graph first, so host launch
@@ -31,8 +33,10 @@ METRIC = "context-KV rows/s (fused GEMM+norm+RoPE+write); % of MFMA/HBM roofline
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
 INFINITY_CACHE_BYTES = 256 << 20
-KERNEL_SOURCE = os.path.join(ROOT, "speculative_decoding_draft_stacked_amd", "csrc",
-                             "ctx_kv_write.hip")
+CSRC = os.path.join(ROOT, "speculative_decoding_draft_stacked_amd", "csrc")
+KERNEL_SOURCE = os.path.join(CSRC, "ctx_kv_write.hip")
+QK_KERNEL_SOURCE = os.path.join(CSRC, "qk_norm_rope.hip")
+QK_METRIC = "in-place QK-RMSNorm+RoPE tokens/s; % of HBM roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_PROBE_BYTES = 1 << 30
 
@@ -55,8 +59,23 @@ def algorithmic(case, written_rows: int) -> dict:
     return {"flops": flops, "bytes": float(nbytes)}
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
+def qk_algorithmic(c) -> dict:
+    """Algorithmic HBM bytes of one in-place QK call: the query and key heads
+    read and written once, one table row and one position per token, the two
+    norm weights."""
+    heads = c.T * (c.NHQ + c.NHK) * c.D * 2
+    wbytes = 4 if c.weight_dtype == "fp32" else 2
+    nbytes = 2 * heads + c.T * c.D * 4 + 8 * c.T + 2 * c.D * wbytes
+    flops = 10.0 * c.T * (c.NHQ + c.NHK) * c.D  # norm + rotation, for the record
+    return {"flops": flops, "bytes": float(nbytes)}
+
+
+def is_qk(workload: str) -> bool:
+    return workload.startswith("qk_")
+
+
+def kernel_source_hash(workload: str = "") -> str:
+    with open(QK_KERNEL_SOURCE if is_qk(workload) else KERNEL_SOURCE, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
@@ -68,7 +87,7 @@ def measured_traffic(workload: str):
             rec = json.load(f).get(workload)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("kernel_sha") != kernel_source_hash():
+    if not rec or rec.get("kernel_sha") != kernel_source_hash(workload):
         return None
     return rec.get("bytes_per_launch")
 
@@ -106,7 +125,7 @@ def record_traffic(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir
     if os.path.exists(TRAFFIC_FILE):
         rec = json.load(open(TRAFFIC_FILE))
     rec[workload] = {
-        "kernel": kernel, "kernel_sha": kernel_source_hash(),
+        "kernel": kernel, "kernel_sha": kernel_source_hash(workload),
         "fetch_kib": fetch, "write_kib": write,
         "fetch_scale": fetch_scale, "write_scale": write_scale,
         "bytes_per_launch": round(fetch * 1024 * fetch_scale + write * 1024 * write_scale),
@@ -153,6 +172,143 @@ def cpu_baseline(case, seconds: float) -> dict:
                       f"layers) in {el:.1f} s; numpy fp64, BLAS threads = {threads}"}
 
 
+def qk_cpu_baseline(c, seconds: float) -> dict:
+    """The QK oracle on the same batch, repeated for about `seconds`."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import qk_norm_rope_oracle as Q
+
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        buf = c.qkv.copy()
+        Q.qk_norm_rope_inplace(buf, c.positions, c.q_w, c.k_w, c.weight_dtype, c.table, c.NHQ,
+                               c.NHK, c.D, c.eps, c.dtype)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": c.T * reps / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{reps} full passes of the {c.name} batch ({c.T} tokens, "
+                      f"{c.NHQ}+{c.NHK} heads) in {el:.1f} s; numpy fp64, BLAS threads = "
+                      f"{threads}"}
+
+
+def time_steps(step, steps: int, warmup: int, eager: bool):
+    """Warm up, then time exactly `steps` calls of step(i) with events on the
+    stream they run on. Returns (device ms, wall s, launch mode)."""
+    import torch
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if eager:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        for i in range(steps):
+            step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1), time.perf_counter() - t0, "eager"
+    side = torch.cuda.Stream()
+    g_warm, g_main = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g_warm, stream=side):
+            for i in range(warmup):
+                step(i)
+        with torch.cuda.graph(g_main, stream=side):
+            for i in range(steps):
+                step(i)
+    g_warm.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    g_main.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1), time.perf_counter() - t0, "hip_graph"
+
+
+def roofline(alg: dict, t_kernel: float, workload: str) -> dict:
+    ridge = MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if alg["flops"] / alg["bytes"] < ridge or is_qk(workload):
+        ach = alg["bytes"] / t_kernel / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    else:
+        ach = alg["flops"] / t_kernel / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_PEAK_TFLOPS, 4)}
+    roof["traffic"] = measured_traffic(workload)
+    return roof
+
+
+def run_qk(args) -> int:
+    """The in-place QK norm + rotation on a QK workload; one call per step.
+    Successive steps use different copies of the QKV tensor, enough to exceed
+    the Infinity Cache, so every step streams its heads from HBM."""
+    import numpy as np
+    import torch
+
+    import speculative_decoding_draft_stacked_amd as dk
+    from speculative_decoding_draft_stacked_amd import workloads as W
+
+    log(f"[bench] generating workload {args.workload}")
+    c = W.qk_workload(args.workload)
+    alg = qk_algorithmic(c)
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16}[c.dtype]
+    base = torch.from_numpy(c.qkv.view(np.int16)).view(tdt).cuda()
+    copies = max(1, math.ceil(2 * INFINITY_CACHE_BYTES / base.numel() / 2))
+    bufs = [base.clone() for _ in range(copies)]
+    if c.weight_dtype == "fp32":
+        qw, kw = torch.from_numpy(c.q_w).cuda(), torch.from_numpy(c.k_w).cuda()
+    else:
+        qw = torch.from_numpy(c.q_w.view(np.int16)).view(tdt).cuda()
+        kw = torch.from_numpy(c.k_w.view(np.int16)).view(tdt).cuda()
+    table = torch.from_numpy(c.table).cuda()
+    pos = torch.from_numpy(c.positions).cuda()
+    err = torch.zeros(1, dtype=torch.int64, device="cuda")
+    log(f"[bench] T={c.T} NHQ={c.NHQ} NHK={c.NHK} D={c.D} {c.dtype}, buffer copies {copies}")
+
+    def step(i):
+        if not dk.table_qk_norm_rope(bufs[i % copies], pos, qw, kw, table, c.NHQ, c.NHK, c.D,
+                                     c.eps, range_errors=err):
+            raise RuntimeError("QK call fell back")
+
+    gpu_ms, wall, launch = time_steps(step, args.steps, args.warmup, args.eager)
+    assert int(err.item()) == 0
+    log(f"[bench] {args.steps} steps: device {gpu_ms:.3f} ms, wall {wall * 1e3:.3f} ms")
+    ms_per_step = gpu_ms / args.steps
+    t_kernel = ms_per_step * 1e-3
+    out = {
+        "metric": QK_METRIC,
+        "value": round(c.T / t_kernel, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": c.dtype,
+        "data": "synthetic: seeded random fused QKV rows, norm weights and positions",
+        "config": {"workload": args.workload, "T": c.T, "q_heads": c.NHQ, "k_heads": c.NHK,
+                   "head_dim": c.D, "row_stride": c.row_stride, "buffer_copies": copies,
+                   "launch": launch, "algorithmic_bytes": alg["bytes"]},
+        "roofline": roofline(alg, t_kernel, args.workload),
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the CPU oracle for ~{args.cpu_seconds} s")
+        out["cpu_baseline"] = qk_cpu_baseline(c, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -195,6 +351,8 @@ def main() -> int:
         return 1
     dk.lib()
     torch.cuda.set_device(0)
+    if is_qk(args.workload):
+        return run_qk(args)
 
     log(f"[bench] generating workload {args.workload}")
     case = W.workload(args.workload)
@@ -222,59 +380,13 @@ def main() -> int:
             raise RuntimeError("write fell back")
 
     # warmup (eager) also validates the launch path before capture
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    if args.eager:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        e0.record()
-        for i in range(args.steps):
-            step(i)
-        e1.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        gpu_ms = e0.elapsed_time(e1)
-        launch = "eager"
-    else:
-        side = torch.cuda.Stream()
-        g_warm, g_main = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-        with torch.cuda.stream(side):
-            with torch.cuda.graph(g_warm, stream=side):
-                for i in range(args.warmup):
-                    step(i)
-            with torch.cuda.graph(g_main, stream=side):
-                for i in range(args.steps):
-                    step(i)
-        g_warm.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        e0.record()
-        g_main.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        gpu_ms = e0.elapsed_time(e1)
-        launch = "hip_graph"
+    gpu_ms, wall, launch = time_steps(step, args.steps, args.warmup, args.eager)
     assert packs[0].range_errors() == 0
     log(f"[bench] {args.steps} steps: device {gpu_ms:.3f} ms, wall {wall * 1e3:.3f} ms")
 
     ms_per_step = gpu_ms / args.steps
     t_kernel = ms_per_step * 1e-3  # one kernel per step
-    ridge = MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if alg["flops"] / alg["bytes"] < ridge:
-        ach = alg["bytes"] / t_kernel / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4)}
-    else:
-        ach = alg["flops"] / t_kernel / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / MFMA_PEAK_TFLOPS, 4)}
-    roof["traffic"] = measured_traffic(args.workload)
+    roof = roofline(alg, t_kernel, args.workload)
 
     out = {
         "metric": METRIC,
