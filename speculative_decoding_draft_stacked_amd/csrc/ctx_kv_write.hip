@@ -11,16 +11,20 @@
 //
 // Tiling. The GEMM is computed transposed, Y^T = W_stacked * X^T: weight rows
 // run along the MFMA M axis and tokens along N, so both operands are K-major
-// in memory and no transpose is needed. A workgroup (4 waves) owns BN = 128
-// weight rows, i.e. one head of 128 or two heads of 64, so a tile never
-// straddles a head and the norm and the (d, d + D/2) rotation pairs are local
-// to it, and BT tokens. The K loop stages 64-wide slices of both operands
-// through double-buffered LDS with rows padded to 144 bytes so that the
-// 16-byte fragment reads of 8 consecutive rows fall on distinct banks.
+// in memory and no transpose is needed. Weight tiles are 128 rows, i.e. one
+// head of 128 or two heads of 64, so a tile never straddles a head and the
+// norm and the (d, d + D/2) rotation pairs are local to it. The weight comes
+// from the pack in a blocked layout where each wave's MFMA A fragment for one
+// 16-wide K step is one contiguous KiB. Two kernels cover the two regimes:
+//   - ctx_kv_stream_kernel, small T: one 128-row tile x up to 128 tokens per
+//     workgroup, the weight streamed from HBM into registers;
+//   - ctx_kv_tiled_kernel, large T: 256 rows x 128/192/256 tokens per
+//     workgroup, both operands staged through an LDS ring by direct-to-LDS
+//     loads.
 // MFMA: v_mfma_f32_32x32x16_{bf16,f16}, fp32 accumulation.
 //
 // Epilogue. Accumulators (+ bias) are rounded once to the dtype (the GEMM's
-// output dtype) into an LDS tile [BT][BN]. Each (token, head) is then handled
+// output dtype) into an LDS tile [BT][rows]. Each (token, head) is then handled
 // by D/16 lanes: every lane owns 8 elements of the first half and their 8
 // rotation partners in the second half, so the rotation needs no exchange and
 // the sum of squares needs log2(D/16) lane swaps. K is normalised in fp32
@@ -37,7 +41,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int BN = 128;       // weight rows per tile
 constexpr int BK = 64;        // K slice per pipeline stage
-constexpr int LDK = BK + 8;   // padded LDS row of an operand tile (elements)
 constexpr int NTHREADS = 256;
 
 template <bool FP16>
@@ -79,14 +82,6 @@ __device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
   typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
   const u32x4 v = *(global_u32x4*)p;
   return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
-// Workgroup barrier that orders LDS only: waits for this wave's LDS accesses,
-// not for its outstanding global loads, so prefetches stay in flight.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 template <typename E>
