@@ -312,3 +312,56 @@ def qk_workload(name: str) -> QkCase:
     """The named QK workload with its fixed seed (2000 + its 1-based index)."""
     seed = 2000 + QK_WORKLOAD_ORDER.index(name) + 1
     return make_qk_case(name=name, seed=seed, **QK_WORKLOADS[name])
+
+
+# ---------------------------------------------------------------------------
+# Inputs of the verify step's accept length and bonus token (sglang PR #31847,
+# implementation breakdown step 2: ``compute_dflash_correct_drafts_and_bonus``):
+# K drafted tokens per request against the target's K + 1 tokens.
+
+
+@dataclasses.dataclass
+class VerifyCase:
+    name: str
+    B: int
+    K: int
+    vocab: int
+    draft: np.ndarray   # int64 [B, K]
+    target: np.ndarray  # int64 [B, K + 1]
+
+
+def make_verify_case(*, name: str = "verify_case", B: int, K: int, vocab: int = 151936,
+                     seed: int = 0, match_len: Optional[np.ndarray] = None) -> VerifyCase:
+    """Draw one case. Order: target tokens, matched-prefix lengths (uniform in
+    [0, K] unless given), replacement tokens. The draft copies the target's
+    first ``match_len[b]`` tokens, then differs at that position (a different
+    token id), then holds random tokens that may or may not match again."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    target = rng.integers(0, vocab, size=(B, K + 1), dtype=np.int64)
+    if match_len is None:
+        match_len = rng.integers(0, K + 1, size=B, dtype=np.int64)
+    match_len = np.asarray(match_len, dtype=np.int64)
+    tail = rng.integers(0, vocab, size=(B, K), dtype=np.int64)
+    draft = target[:, :K].copy()
+    cols = np.arange(K)[None, :]
+    after = cols > match_len[:, None]
+    draft = np.where(after, tail, draft)
+    at = cols == match_len[:, None]
+    shift = 1 + rng.integers(0, vocab - 1, size=(B, K), dtype=np.int64)
+    draft = np.where(at, (target[:, :K] + shift) % vocab, draft)  # never equal at the mismatch
+    return VerifyCase(name=name, B=B, K=K, vocab=vocab, draft=draft, target=target)
+
+
+# Verify workloads: a decode step of 32 requests x 7 drafts (blocks of 8), and
+# a wide batch of 4096 requests x 15 drafts.
+VERIFY_WORKLOADS = {
+    "verify_decode": dict(B=32, K=7),
+    "verify_wide": dict(B=4096, K=15),
+}
+VERIFY_WORKLOAD_ORDER = ["verify_decode", "verify_wide"]
+
+
+def verify_workload(name: str) -> VerifyCase:
+    """The named verify workload with its fixed seed (3000 + its 1-based index)."""
+    seed = 3000 + VERIFY_WORKLOAD_ORDER.index(name) + 1
+    return make_verify_case(name=name, seed=seed, **VERIFY_WORKLOADS[name])
