@@ -206,6 +206,26 @@ int dspark_table_qk_norm_rope(void* qkv, int64_t num_tokens, int64_t row_stride,
                               unsigned long long* range_errors, void* stream,
                               int32_t* fallback_reason);
 
+/* Accept length and bonus token of the verify step (sglang PR #31847,
+ * implementation breakdown step 2: compute_dflash_correct_drafts_and_bonus).
+ *   draft_tokens: device int64 [num_requests, num_drafts], row stride
+ *     draft_row_stride (>= num_drafts); may be NULL when num_drafts == 0.
+ *   target_tokens: device int64 [num_requests, num_drafts + 1], row stride
+ *     target_row_stride (>= num_drafts + 1): the target model's token at each
+ *     verified position.
+ *   accept_lens, bonus_tokens: device int64 [num_requests], written.
+ * accept_lens[b] = length of the longest prefix of request b's drafts equal to
+ * its target tokens (the first mismatching position, num_drafts when none);
+ * bonus_tokens[b] = target_tokens[b][accept_lens[b]]. Exact integer compares.
+ * num_requests == 0 returns DSPARK_OK with nothing enqueued. Enqueued on
+ * `stream`; allocates nothing and does not synchronise.
+ * Returns DSPARK_OK, DSPARK_E_INVALID (negative sizes, short strides, NULL
+ * pointers with work to do) or DSPARK_E_DEVICE. */
+int dspark_verify_accept(const int64_t* draft_tokens, int64_t draft_row_stride,
+                         const int64_t* target_tokens, int64_t target_row_stride,
+                         int64_t num_requests, int32_t num_drafts, int64_t* accept_lens,
+                         int64_t* bonus_tokens, void* stream);
+
 /* Reads and clears the pack's count of rows skipped for an out-of-range
  * position or slot. Synchronises `stream`. Returns DSPARK_OK or an error. */
 int dspark_pack_range_errors(const dspark_ctx_kv_pack* pack, void* stream, int64_t* count);

@@ -32,6 +32,7 @@ EXPORTS = [
     "dspark_check_eligibility", "dspark_pack_ctx_kv", "dspark_ctx_kv_write",
     "dspark_pack_range_errors", "dspark_pack_info", "dspark_pack_buffers", "dspark_pack_free",
     "dspark_status_str", "dspark_fallback_str", "dspark_table_qk_norm_rope",
+    "dspark_verify_accept",
 ]
 
 
@@ -102,6 +103,7 @@ def lib() -> ctypes.CDLL:
                                           ctypes.POINTER(vp)]
         L.dspark_table_qk_norm_rope.argtypes = [vp, i64, i64, vp, i32, i32, i32, i32, vp, vp,
                                                 i32, ctypes.c_double, vp, i64, vp, vp, p_i32]
+        L.dspark_verify_accept.argtypes = [vp, i64, vp, i64, i64, i32, vp, vp, vp]
         L.dspark_pack_free.argtypes = [vp]
         L.dspark_pack_free.restype = None
         L.dspark_status_str.argtypes = [ctypes.c_int]
@@ -110,7 +112,7 @@ def lib() -> ctypes.CDLL:
         L.dspark_fallback_str.restype = ctypes.c_char_p
         for name in ("dspark_check_eligibility", "dspark_pack_ctx_kv", "dspark_ctx_kv_write",
                      "dspark_pack_range_errors", "dspark_pack_info", "dspark_pack_buffers",
-                     "dspark_table_qk_norm_rope"):
+                     "dspark_table_qk_norm_rope", "dspark_verify_accept"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -319,3 +321,31 @@ def table_qk_norm_rope(qkv, positions, q_norm_weight, k_norm_weight, cos_sin_cac
         return False
     _raise_for(st, "dspark_table_qk_norm_rope")
     return True
+
+
+def verify_accept_raw(draft: Optional[int], draft_row_stride: int, target: int,
+                      target_row_stride: int, num_requests: int, num_drafts: int, accept: int,
+                      bonus: int, stream) -> int:
+    """dspark_verify_accept on raw device pointers; returns the status."""
+    return lib().dspark_verify_accept(draft, draft_row_stride, target, target_row_stride,
+                                      num_requests, num_drafts, accept, bonus, _stream(stream))
+
+
+def verify_accept(draft, target, accept, bonus, stream=None) -> None:
+    """Enqueue accept lengths and bonus tokens: ``draft`` int64 [B, K],
+    ``target`` int64 [B, K + 1] (unit column stride), ``accept`` and ``bonus``
+    int64 [B] outputs. ValueError on misuse."""
+    import torch
+    for name, t in (("draft", draft), ("target", target), ("accept", accept), ("bonus", bonus)):
+        if t.dtype != torch.int64:
+            raise ValueError(f"{name} must be int64")
+    if draft.dim() != 2 or target.dim() != 2 or (draft.numel() and draft.stride(1) != 1) or \
+            target.stride(1) != 1:
+        raise ValueError("draft and target must be [B, K] / [B, K + 1] with unit column stride")
+    B, K = draft.shape
+    if target.shape[0] != B or target.shape[1] != K + 1 or accept.numel() < B or bonus.numel() < B:
+        raise ValueError("shape mismatch")
+    st = verify_accept_raw(draft.data_ptr() if K else None, draft.stride(0) if K else 0,
+                           target.data_ptr(), target.stride(0), B, K, accept.data_ptr(),
+                           bonus.data_ptr(), stream)
+    _raise_for(st, "dspark_verify_accept")

@@ -295,6 +295,30 @@ int dspark_table_qk_norm_rope(void* qkv, int64_t num_tokens, int64_t row_stride,
   return e == hipSuccess ? DSPARK_OK : DSPARK_E_DEVICE;
 }
 
+int dspark_verify_accept(const int64_t* draft_tokens, int64_t draft_row_stride,
+                         const int64_t* target_tokens, int64_t target_row_stride,
+                         int64_t num_requests, int32_t num_drafts, int64_t* accept_lens,
+                         int64_t* bonus_tokens, void* stream_ptr) {
+  if (num_requests < 0 || num_drafts < 0) return DSPARK_E_INVALID;
+  if (draft_row_stride < num_drafts || target_row_stride < (int64_t)num_drafts + 1)
+    return DSPARK_E_INVALID;
+  if (num_requests == 0) return DSPARK_OK;
+  if ((num_drafts > 0 && !draft_tokens) || !target_tokens || !accept_lens || !bonus_tokens)
+    return DSPARK_E_INVALID;
+  dspark::VerifyArgs a = {};
+  a.draft = draft_tokens;
+  a.target = target_tokens;
+  a.draft_stride = draft_row_stride;
+  a.target_stride = target_row_stride;
+  a.B = num_requests;
+  a.accept = accept_lens;
+  a.bonus = bonus_tokens;
+  a.K = num_drafts;
+  const hipError_t e =
+      dspark::launch_verify_accept(a, static_cast<hipStream_t>(stream_ptr));
+  return e == hipSuccess ? DSPARK_OK : DSPARK_E_DEVICE;
+}
+
 int dspark_pack_range_errors(const dspark_ctx_kv_pack* p, void* stream_ptr, int64_t* count) {
   if (!p || !count) return DSPARK_E_INVALID;
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);

@@ -59,6 +59,23 @@ struct QkArgs {
 hipError_t launch_qk_norm_rope(const QkArgs& a, int head_dim, bool is_fp16, bool weight_fp32,
                                hipStream_t stream);
 
+// Arguments of the verify accept length + bonus token.
+struct VerifyArgs {
+  const int64_t* draft;     // [B, >= K] drafted tokens
+  const int64_t* target;    // [B, >= K + 1] target tokens
+  int64_t draft_stride;     // elements between requests
+  int64_t target_stride;
+  int64_t B;
+  int64_t* accept;          // [B]
+  int64_t* bonus;           // [B]
+  int32_t K;
+  int32_t lanes_per_request;  // set by the launcher
+};
+
+// Launches the verify accept/bonus kernel for `a` on `stream` (validated by
+// the caller). Returns the launch status.
+hipError_t launch_verify_accept(const VerifyArgs& a, hipStream_t stream);
+
 // Launches the fused GEMM + norm + rotation + scatter for `a` on `stream`.
 // `num_cus` (compute units of the device) sizes the small-T grid. Shapes have
 // been validated by the caller. Returns the launch status.

@@ -181,3 +181,21 @@ def test_qk_weight_dtype_may_be_fp32():
     # passes the dtype checks and stops at the NULL pointers
     assert _qk(wdt=dk.FP32) == (dk.E_INVALID, 0)
     assert _qk(act=dk.FP16, wdt=dk.FP32) == (dk.E_INVALID, 0)
+
+
+# ------------------------------------------------ verify accept length + bonus
+
+def _verify(B=4, K=7, ds=7, ts=8, d=None, t=None, acc=None, bon=None):
+    """NULL device pointers: only host-side checks may run."""
+    return dk.lib().dspark_verify_accept(d, ds, t, ts, B, K, acc, bon, None)
+
+
+def test_verify_empty_is_ok():
+    assert _verify(B=0) == dk.OK
+
+
+@pytest.mark.parametrize("kw", [
+    dict(B=-1), dict(K=-1), dict(ds=6), dict(ts=7), dict(),  # last: NULL pointers with work
+])
+def test_verify_invalid_arguments(kw):
+    assert _verify(**kw) == dk.E_INVALID
