@@ -5,7 +5,8 @@ One step = one dspark_ctx_kv_write over one batch of the workload (GEMM + K
 RMSNorm + neox RoPE + scatter into every layer's pool), inputs resident in HBM.
 Prints ONE JSON line on stdout; progress goes to stderr. The workloads
 qk_decode and qk_prefill_8k time the in-place table QK-RMSNorm + neox RoPE
-(dspark_table_qk_norm_rope) instead, one call per step.
+(dspark_table_qk_norm_rope) instead, one call per step, and verify_decode and
+verify_wide time the accept length + bonus token (dspark_verify_accept).
 
 Timing: W warmup steps, then exactly K steps, each bracketed by a device
 synchronisation. The steps are captured into a HIP graph first, so host launch
@@ -37,6 +38,8 @@ CSRC = os.path.join(ROOT, "speculative_decoding_draft_stacked_amd", "csrc")
 KERNEL_SOURCE = os.path.join(CSRC, "ctx_kv_write.hip")
 QK_KERNEL_SOURCE = os.path.join(CSRC, "qk_norm_rope.hip")
 QK_METRIC = "in-place QK-RMSNorm+RoPE tokens/s; % of HBM roofline"
+VERIFY_KERNEL_SOURCE = os.path.join(CSRC, "verify_accept.hip")
+VERIFY_METRIC = "verify accept-length + bonus requests/s; % of HBM roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_PROBE_BYTES = 1 << 30
 
@@ -74,8 +77,14 @@ def is_qk(workload: str) -> bool:
     return workload.startswith("qk_")
 
 
+def is_verify(workload: str) -> bool:
+    return workload.startswith("verify_")
+
+
 def kernel_source_hash(workload: str = "") -> str:
-    with open(QK_KERNEL_SOURCE if is_qk(workload) else KERNEL_SOURCE, "rb") as f:
+    src = (QK_KERNEL_SOURCE if is_qk(workload) else
+           VERIFY_KERNEL_SOURCE if is_verify(workload) else KERNEL_SOURCE)
+    with open(src, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
@@ -235,7 +244,7 @@ def time_steps(step, steps: int, warmup: int, eager: bool):
 
 def roofline(alg: dict, t_kernel: float, workload: str) -> dict:
     ridge = MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if alg["flops"] / alg["bytes"] < ridge or is_qk(workload):
+    if alg["flops"] / alg["bytes"] < ridge or is_qk(workload) or is_verify(workload):
         ach = alg["bytes"] / t_kernel / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4)}
@@ -309,6 +318,63 @@ def run_qk(args) -> int:
     return 0
 
 
+def run_verify(args) -> int:
+    """Verify accept length + bonus token on a verify workload; one call per
+    step. Algorithmic bytes: the draft and target tokens read once, the two
+    outputs written once (int64 each)."""
+    import time as _t
+
+    import numpy as np
+    import torch
+
+    import speculative_decoding_draft_stacked_amd as dk
+    from speculative_decoding_draft_stacked_amd import workloads as W
+
+    c = W.verify_workload(args.workload)
+    nbytes = float(8 * c.B * (2 * c.K + 1) + 16 * c.B)
+    alg = {"flops": 0.0, "bytes": nbytes}
+    d = torch.from_numpy(c.draft).cuda()
+    t = torch.from_numpy(c.target).cuda()
+    acc = torch.empty(c.B, dtype=torch.int64, device="cuda")
+    bon = torch.empty(c.B, dtype=torch.int64, device="cuda")
+    log(f"[bench] B={c.B} K={c.K}")
+
+    def step(i):
+        dk.verify_accept(d, t, acc, bon)
+
+    gpu_ms, wall, launch = time_steps(step, args.steps, args.warmup, args.eager)
+    ms_per_step = gpu_ms / args.steps
+    t_kernel = ms_per_step * 1e-3
+    out = {
+        "metric": VERIFY_METRIC, "value": round(c.B / t_kernel, 1), "unit": "requests/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int64",
+        "data": "synthetic: seeded token ids with a uniform matched-prefix length",
+        "config": {"workload": args.workload, "requests": c.B, "drafts": c.K, "launch": launch,
+                   "algorithmic_bytes": nbytes},
+        "roofline": roofline(alg, t_kernel, args.workload),
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+        from oracle import verify_oracle as V
+        reps, t0 = 0, _t.perf_counter()
+        while True:
+            V.accept_and_bonus(c.draft, c.target)
+            reps += 1
+            el = _t.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        out["cpu_baseline"] = {"value": c.B * reps / el, "unit": "requests/s",
+                               "cores": int(threads), "kind": "oracle",
+                               "sample": f"{reps} passes of the {c.name} batch ({c.B} requests "
+                                         f"x {c.K} drafts) in {el:.1f} s; numpy cumprod"}
+    del np
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -353,6 +419,8 @@ def main() -> int:
     torch.cuda.set_device(0)
     if is_qk(args.workload):
         return run_qk(args)
+    if is_verify(args.workload):
+        return run_verify(args)
 
     log(f"[bench] generating workload {args.workload}")
     case = W.workload(args.workload)
