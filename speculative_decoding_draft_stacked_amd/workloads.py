@@ -365,3 +365,61 @@ def verify_workload(name: str) -> VerifyCase:
     """The named verify workload with its fixed seed (3000 + its 1-based index)."""
     seed = 3000 + VERIFY_WORKLOAD_ORDER.index(name) + 1
     return make_verify_case(name=name, seed=seed, **VERIFY_WORKLOADS[name])
+
+
+# ---------------------------------------------------------------------------
+# Inputs of the context producer ctx_hidden = main_norm(main_proj(aux)) (vLLM
+# PR #46995, key source snippets: ``combine_hidden_states``): the target's
+# auxiliary hidden states of n layers concatenated to [T, n*H], a bias-free
+# [H, n*H] projection and an RMSNorm weight [H].
+
+
+@dataclasses.dataclass
+class ProjCase:
+    name: str
+    dtype: str
+    T: int
+    H: int        # output features (the draft's hidden size)
+    n_aux: int    # number of target layers concatenated
+    eps: float
+    g_dtype: str  # norm weight dtype: the activation dtype or "fp32"
+    aux: np.ndarray  # uint16 [T, n_aux * H]
+    w: np.ndarray    # uint16 [H, n_aux * H]
+    g: np.ndarray    # [H] patterns, or float32
+
+    @property
+    def K(self) -> int:
+        return self.n_aux * self.H
+
+
+def make_proj_case(*, name: str = "proj_case", T: int, H: int, n_aux: int = 3,
+                   dtype: str = BF16, eps: float = 1e-6, g_fp32: bool = False,
+                   seed: int = 0, aux_std: float = 1.0) -> ProjCase:
+    """Draw one case. Order: aux, weight, norm weight. aux ~ N(0, aux_std) with a
+    per-row scale e^N(0, 0.5) (row RMS values differ, which the norm removes);
+    weight ~ N(0, 1/sqrt(n*H)) so that projected values are O(1); norm weight
+    1 + N(0, 0.1)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    K = n_aux * H
+    aux = rng.standard_normal((T, K)) * aux_std * np.exp(rng.standard_normal((T, 1)) * 0.5)
+    w = rng.standard_normal((H, K)) / np.sqrt(K)
+    g = 1.0 + rng.standard_normal(H) * 0.1
+    return ProjCase(name=name, dtype=dtype, T=T, H=H, n_aux=n_aux, eps=eps,
+                    g_dtype="fp32" if g_fp32 else dtype, aux=to_bits(aux, dtype),
+                    w=to_bits(w, dtype),
+                    g=g.astype(np.float32) if g_fp32 else to_bits(g, dtype))
+
+
+# Producer workloads: three target layers of a 4096-wide model (the
+# decode_commit / prefill_8k shapes of the write), 256 and 8192 tokens.
+PROJ_WORKLOADS = {
+    "proj_decode": dict(T=256, H=4096, n_aux=3),
+    "proj_prefill_8k": dict(T=8192, H=4096, n_aux=3),
+}
+PROJ_WORKLOAD_ORDER = ["proj_decode", "proj_prefill_8k"]
+
+
+def proj_workload(name: str) -> ProjCase:
+    """The named producer workload with its fixed seed (4000 + its 1-based index)."""
+    seed = 4000 + PROJ_WORKLOAD_ORDER.index(name) + 1
+    return make_proj_case(name=name, seed=seed, **PROJ_WORKLOADS[name])
