@@ -6,7 +6,8 @@ RMSNorm + neox RoPE + scatter into every layer's pool), inputs resident in HBM.
 Prints ONE JSON line on stdout; progress goes to stderr. The workloads
 qk_decode and qk_prefill_8k time the in-place table QK-RMSNorm + neox RoPE
 (dspark_table_qk_norm_rope) instead, one call per step, and verify_decode and
-verify_wide time the accept length + bonus token (dspark_verify_accept).
+verify_wide time the accept length + bonus token (dspark_verify_accept), and
+proj_decode and proj_prefill_8k the context producer (dspark_main_proj_norm).
 
 Timing: W warmup steps, then exactly K steps, each bracketed by a device
 synchronisation. The steps are captured into a HIP graph first, so host launch
@@ -39,6 +40,7 @@ KERNEL_SOURCE = os.path.join(CSRC, "ctx_kv_write.hip")
 QK_KERNEL_SOURCE = os.path.join(CSRC, "qk_norm_rope.hip")
 QK_METRIC = "in-place QK-RMSNorm+RoPE tokens/s; % of HBM roofline"
 VERIFY_KERNEL_SOURCE = os.path.join(CSRC, "verify_accept.hip")
+PROJ_METRIC = "context-producer tokens/s (main_proj GEMM + main_norm); % of MFMA/HBM roofline"
 VERIFY_METRIC = "verify accept-length + bonus requests/s; % of HBM roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_PROBE_BYTES = 1 << 30
@@ -79,6 +81,10 @@ def is_qk(workload: str) -> bool:
 
 def is_verify(workload: str) -> bool:
     return workload.startswith("verify_")
+
+
+def is_proj(workload: str) -> bool:
+    return workload.startswith("proj_")
 
 
 def kernel_source_hash(workload: str = "") -> str:
@@ -375,6 +381,74 @@ def run_verify(args) -> int:
     return 0
 
 
+def run_proj(args) -> int:
+    """The context producer main_norm(main_proj(aux)) on a proj workload; one
+    dspark_main_proj_norm (projection GEMM + row norm, two launches) per step,
+    rotating over packed weight copies that exceed the Infinity Cache.
+    Algorithmic FLOPs 2*T*H*K; bytes = weight + aux read + ctx written + norm
+    weight (the norm's in-place pass over ctx is this implementation's, not
+    the method's, and is not counted)."""
+    import numpy as np
+    import torch
+
+    import speculative_decoding_draft_stacked_amd as dk
+    from speculative_decoding_draft_stacked_amd import workloads as W
+
+    c = W.proj_workload(args.workload)
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16}[c.dtype]
+    dev16 = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(tdt).cuda()
+    aux, w = dev16(c.aux), dev16(c.w)
+    g = torch.from_numpy(c.g).cuda() if c.g_dtype == "fp32" else dev16(c.g)
+    w_bytes = c.H * c.K * 2
+    copies = max(1, math.ceil(2 * INFINITY_CACHE_BYTES / w_bytes))
+    packs = [dk.pack_main_proj(w, g, c.eps) for _ in range(copies)]
+    del w
+    ctx = torch.empty(c.T, c.H, dtype=tdt, device="cuda")
+    ws = torch.empty(packs[0].workspace_bytes(c.T), dtype=torch.uint8, device="cuda")
+    flops = 2.0 * c.T * c.H * c.K
+    nbytes = float(w_bytes + c.T * c.K * 2 + c.T * c.H * 2 + c.H * 4)
+    alg = {"flops": flops, "bytes": nbytes}
+    log(f"[bench] T={c.T} H={c.H} n_aux={c.n_aux} {c.dtype}, weight copies {copies}")
+
+    def step(i):
+        dk.main_proj_norm(packs[i % copies], aux, ctx, ws)
+
+    gpu_ms, wall, launch = time_steps(step, args.steps, args.warmup, args.eager)
+    ms_per_step = gpu_ms / args.steps
+    t_kernel = ms_per_step * 1e-3
+    out = {
+        "metric": PROJ_METRIC, "value": round(c.T / t_kernel, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": c.dtype,
+        "data": "synthetic: seeded auxiliary hidden states and random-init projection weights",
+        "config": {"workload": args.workload, "T": c.T, "H": c.H, "n_aux": c.n_aux,
+                   "weight_copies": copies, "launch": launch, "launches_per_step": 2,
+                   "algorithmic_bytes": nbytes, "flops": flops},
+        "roofline": roofline(alg, t_kernel, args.workload),
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+        from oracle import main_proj_oracle as M
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            M.combine_hidden_states(c.aux, c.w, c.g, c.g_dtype, c.eps, c.dtype)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        out["cpu_baseline"] = {"value": c.T * reps / el, "unit": "tokens/s", "cores": int(threads),
+                               "kind": "oracle",
+                               "sample": f"{reps} full passes of the {c.name} batch ({c.T} "
+                                         f"tokens) in {el:.1f} s; numpy fp64, BLAS threads = "
+                                         f"{threads}"}
+    for p in packs:
+        p.free()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -421,6 +495,8 @@ def main() -> int:
         return run_qk(args)
     if is_verify(args.workload):
         return run_verify(args)
+    if is_proj(args.workload):
+        return run_proj(args)
 
     log(f"[bench] generating workload {args.workload}")
     case = W.workload(args.workload)

@@ -226,6 +226,58 @@ int dspark_verify_accept(const int64_t* draft_tokens, int64_t draft_row_stride,
                          int64_t num_requests, int32_t num_drafts, int64_t* accept_lens,
                          int64_t* bonus_tokens, void* stream);
 
+/* ---------------------------------------------------------- context producer
+ * ctx_hidden = main_norm(main_proj(aux)) (vLLM PR #46995, key source snippets:
+ * DSparkDeepseekV4Model.combine_hidden_states): the target's auxiliary hidden
+ * states of n layers, concatenated to aux [T, n*H], go through a bias-free
+ * linear main_proj (weight [H, n*H]) and an RMSNorm main_norm over the H
+ * features: y = round(aux @ W^T), ctx = round(y * inv * g) with
+ * inv = 1 / sqrt(mean(y^2) + eps) in fp32 and g the norm weight widened to
+ * fp32; both roundings are round-to-nearest-even into the activation dtype. */
+typedef struct dspark_main_proj_pack dspark_main_proj_pack; /* opaque */
+
+/* Packs the projection once. weight: device [out_features, in_features] in
+ * w_dtype, row stride w_row_stride (elements, >= in_features), 16-byte
+ * aligned. norm_weight: device [out_features] in act_dtype or fp32. Copies
+ * both (the weight into the library's blocked layout, see dspark_pack_buffers;
+ * the norm weight widened to fp32), synchronises `stream`, and keeps no
+ * reference to the sources.
+ * Returns DSPARK_OK with *out set; DSPARK_FALLBACK with *fallback_reason
+ * (may be NULL) = DSPARK_FB_DTYPE (act_dtype not bf16/fp16, norm weight dtype
+ * not act_dtype/fp32), DSPARK_FB_NOT_SLICEABLE (w_dtype != act_dtype) or
+ * DSPARK_FB_SHAPE (out_features % 128, in_features % 8, w_row_stride % 8 or
+ * weight alignment); DSPARK_E_INVALID (NULL pointers or out, non-positive
+ * sizes, short row stride, eps negative or not finite); DSPARK_E_NOMEM;
+ * DSPARK_E_DEVICE. */
+int dspark_pack_main_proj(const void* weight, int64_t out_features, int64_t in_features,
+                          int64_t w_row_stride, int32_t w_dtype, const void* norm_weight,
+                          int32_t norm_weight_dtype, double eps, int32_t act_dtype, void* stream,
+                          dspark_main_proj_pack** out, int32_t* fallback_reason);
+
+/* Device workspace bytes dspark_main_proj_norm needs for num_tokens tokens
+ * (one fp32 per token and 128-feature group). Host-only. */
+int dspark_main_proj_workspace_bytes(const dspark_main_proj_pack* pack, int64_t num_tokens,
+                                     int64_t* bytes);
+
+/* The producer for num_tokens tokens: aux_hidden device [num_tokens,
+ * in_features] (row stride aux_row_stride >= in_features, a multiple of 8,
+ * 16-byte aligned) -> ctx_hidden device [num_tokens, out_features] (row stride
+ * ctx_row_stride, same rules), written whole. workspace: device, 16-byte
+ * aligned, at least dspark_main_proj_workspace_bytes; its contents are
+ * scratch (no need to clear; calls sharing a workspace on different streams
+ * race). Two launches on `stream` (the projection, then the row norm in place
+ * on ctx_hidden); allocates nothing and does not synchronise.
+ * num_tokens == 0 returns DSPARK_OK with nothing enqueued.
+ * Returns DSPARK_OK, DSPARK_E_INVALID (NULL pointers with work to do, strides,
+ * alignment, workspace too small, pack of another device) or DSPARK_E_DEVICE. */
+int dspark_main_proj_norm(const dspark_main_proj_pack* pack, const void* aux_hidden,
+                          int64_t num_tokens, int64_t aux_row_stride, void* ctx_hidden,
+                          int64_t ctx_row_stride, void* workspace, int64_t workspace_bytes,
+                          void* stream);
+
+/* Frees the producer pack (waits for the device first). NULL is a no-op. */
+void dspark_main_proj_free(dspark_main_proj_pack* pack);
+
 /* Reads and clears the pack's count of rows skipped for an out-of-range
  * position or slot. Synchronises `stream`. Returns DSPARK_OK or an error. */
 int dspark_pack_range_errors(const dspark_ctx_kv_pack* pack, void* stream, int64_t* count);

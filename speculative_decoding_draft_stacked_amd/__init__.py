@@ -32,7 +32,8 @@ EXPORTS = [
     "dspark_check_eligibility", "dspark_pack_ctx_kv", "dspark_ctx_kv_write",
     "dspark_pack_range_errors", "dspark_pack_info", "dspark_pack_buffers", "dspark_pack_free",
     "dspark_status_str", "dspark_fallback_str", "dspark_table_qk_norm_rope",
-    "dspark_verify_accept",
+    "dspark_verify_accept", "dspark_pack_main_proj", "dspark_main_proj_workspace_bytes",
+    "dspark_main_proj_norm", "dspark_main_proj_free",
 ]
 
 
@@ -104,6 +105,12 @@ def lib() -> ctypes.CDLL:
         L.dspark_table_qk_norm_rope.argtypes = [vp, i64, i64, vp, i32, i32, i32, i32, vp, vp,
                                                 i32, ctypes.c_double, vp, i64, vp, vp, p_i32]
         L.dspark_verify_accept.argtypes = [vp, i64, vp, i64, i64, i32, vp, vp, vp]
+        L.dspark_pack_main_proj.argtypes = [vp, i64, i64, i64, i32, vp, i32, ctypes.c_double,
+                                            i32, vp, ctypes.POINTER(vp), p_i32]
+        L.dspark_main_proj_workspace_bytes.argtypes = [vp, i64, p_i64]
+        L.dspark_main_proj_norm.argtypes = [vp, vp, i64, i64, vp, i64, vp, i64, vp]
+        L.dspark_main_proj_free.argtypes = [vp]
+        L.dspark_main_proj_free.restype = None
         L.dspark_pack_free.argtypes = [vp]
         L.dspark_pack_free.restype = None
         L.dspark_status_str.argtypes = [ctypes.c_int]
@@ -112,7 +119,9 @@ def lib() -> ctypes.CDLL:
         L.dspark_fallback_str.restype = ctypes.c_char_p
         for name in ("dspark_check_eligibility", "dspark_pack_ctx_kv", "dspark_ctx_kv_write",
                      "dspark_pack_range_errors", "dspark_pack_info", "dspark_pack_buffers",
-                     "dspark_table_qk_norm_rope", "dspark_verify_accept"):
+                     "dspark_table_qk_norm_rope", "dspark_verify_accept",
+                     "dspark_pack_main_proj", "dspark_main_proj_workspace_bytes",
+                     "dspark_main_proj_norm"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -349,3 +358,71 @@ def verify_accept(draft, target, accept, bonus, stream=None) -> None:
                            target.data_ptr(), target.stride(0), B, K, accept.data_ptr(),
                            bonus.data_ptr(), stream)
     _raise_for(st, "dspark_verify_accept")
+
+
+class ProjPack:
+    """A packed context producer (owns device buffers until free())."""
+
+    def __init__(self, handle: int, out_features: int, in_features: int):
+        self.handle = handle
+        self.out_features = out_features
+        self.in_features = in_features
+
+    @property
+    def as_parameter(self):
+        return ctypes.c_void_p(self.handle)
+
+    def workspace_bytes(self, num_tokens: int) -> int:
+        n = ctypes.c_int64(0)
+        _raise_for(lib().dspark_main_proj_workspace_bytes(self.as_parameter, num_tokens,
+                                                          ctypes.byref(n)),
+                   "dspark_main_proj_workspace_bytes")
+        return n.value
+
+    def free(self):
+        if self.handle:
+            lib().dspark_main_proj_free(self.as_parameter)
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def pack_main_proj(weight, norm_weight, eps: float, stream=None):
+    """Pack main_proj ([out, in] weight, unit column stride) and main_norm's
+    weight. Returns a ProjPack, or None on fallback (reason in
+    ``last_fallback_reason``)."""
+    global last_fallback_reason
+    if weight.dim() != 2 or weight.stride(1) != 1:
+        raise ValueError("weight must be [out_features, in_features] with unit column stride")
+    h = ctypes.c_void_p(0)
+    reason = ctypes.c_int32(0)
+    st = lib().dspark_pack_main_proj(weight.data_ptr(), weight.shape[0], weight.shape[1],
+                                     weight.stride(0), _dtype_code(weight),
+                                     norm_weight.data_ptr(), _dtype_code(norm_weight), eps,
+                                     _dtype_code(weight), _stream(stream), ctypes.byref(h),
+                                     ctypes.byref(reason))
+    last_fallback_reason = reason.value
+    if st == FALLBACK:
+        return None
+    _raise_for(st, "dspark_pack_main_proj")
+    return ProjPack(h.value, weight.shape[0], weight.shape[1])
+
+
+def main_proj_norm(pack: ProjPack, aux_hidden, ctx_hidden, workspace, stream=None) -> None:
+    """Enqueue ctx_hidden = main_norm(main_proj(aux_hidden)); ``workspace`` is a
+    device tensor of at least pack.workspace_bytes(T) bytes."""
+    if aux_hidden.stride(1) != 1 or ctx_hidden.stride(1) != 1:
+        raise ValueError("aux_hidden and ctx_hidden need unit column stride")
+    T = aux_hidden.shape[0]
+    if ctx_hidden.shape[0] != T:
+        raise ValueError("token counts differ")
+    st = lib().dspark_main_proj_norm(pack.as_parameter, aux_hidden.data_ptr(), T,
+                                     aux_hidden.stride(0), ctx_hidden.data_ptr(),
+                                     ctx_hidden.stride(0), workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(),
+                                     _stream(stream))
+    _raise_for(st, "dspark_main_proj_norm")

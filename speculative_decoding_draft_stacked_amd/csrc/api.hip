@@ -242,6 +242,7 @@ int dspark_ctx_kv_write(const dspark_ctx_kv_pack* p, const void* ctx_hidden, int
   a.H = (int32_t)p->hidden;
   a.L = p->num_layers;
   a.NH = (int32_t)NH;
+  a.R = (int64_t)p->num_layers * 2 * p->kv_size / 128;
   a.eps = p->eps;
   const hipError_t e = dspark::launch_ctx_kv_write(a, (int)D, p->dtype == DSPARK_FP16,
                                                    p->has_bias != 0, has_commit, p->num_cus,
@@ -391,3 +392,134 @@ const char* dspark_fallback_str(int reason) {
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------ context producer
+
+struct dspark_main_proj_pack {
+  int device = -1;
+  int num_cus = 0;
+  int64_t out_features = 0;  // H
+  int64_t in_features = 0;   // n * H
+  int32_t dtype = DSPARK_BF16;
+  float eps = 0.0f;
+  uint16_t* w = nullptr;     // blocked projection weight
+  float* g = nullptr;        // [H] fp32 norm weight
+  uint16_t* zeros = nullptr;  // 256 zero bytes read by out-of-range K lanes
+};
+
+namespace {
+void free_proj(dspark_main_proj_pack* p) {
+  if (!p) return;
+  (void)hipDeviceSynchronize();
+  if (p->w) (void)hipFree(p->w);
+  if (p->g) (void)hipFree(p->g);
+  if (p->zeros) (void)hipFree(p->zeros);
+  delete p;
+}
+}  // namespace
+
+int dspark_pack_main_proj(const void* weight, int64_t out_features, int64_t in_features,
+                          int64_t w_row_stride, int32_t w_dtype, const void* norm_weight,
+                          int32_t norm_weight_dtype, double eps, int32_t act_dtype,
+                          void* stream_ptr, dspark_main_proj_pack** out,
+                          int32_t* fallback_reason) {
+  set_reason(fallback_reason, DSPARK_FB_NONE);
+  if (!out) return DSPARK_E_INVALID;
+  *out = nullptr;
+  if (!weight || !norm_weight || out_features <= 0 || in_features <= 0 ||
+      w_row_stride < in_features || !(eps >= 0.0) || eps > 3.0e38)
+    return DSPARK_E_INVALID;
+  if (act_dtype != DSPARK_BF16 && act_dtype != DSPARK_FP16)
+    return fallback(fallback_reason, DSPARK_FB_DTYPE);
+  if (w_dtype != act_dtype) return fallback(fallback_reason, DSPARK_FB_NOT_SLICEABLE);
+  if (norm_weight_dtype != act_dtype && norm_weight_dtype != DSPARK_FP32)
+    return fallback(fallback_reason, DSPARK_FB_DTYPE);
+  if (out_features % 128 != 0 || in_features % 8 != 0 || w_row_stride % 8 != 0 ||
+      reinterpret_cast<uintptr_t>(weight) % 16 != 0)
+    return fallback(fallback_reason, DSPARK_FB_SHAPE);
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  dspark_main_proj_pack* p = new (std::nothrow) dspark_main_proj_pack();
+  if (!p) return DSPARK_E_NOMEM;
+  if (hipGetDevice(&p->device) != hipSuccess ||
+      hipDeviceGetAttribute(&p->num_cus, hipDeviceAttributeMultiprocessorCount, p->device) !=
+          hipSuccess) {
+    delete p;
+    return DSPARK_E_DEVICE;
+  }
+  p->out_features = out_features;
+  p->in_features = in_features;
+  p->dtype = act_dtype;
+  p->eps = (float)eps;
+  const int64_t nk = (in_features + 63) / 64;
+  uint16_t* plain = nullptr;
+  auto fail = [&](int s) {
+    if (plain) (void)hipFree(plain);
+    free_proj(p);
+    return s;
+  };
+  if (hipMalloc(&p->w, (size_t)(out_features * nk * 64 * 2)) != hipSuccess ||
+      hipMalloc(&plain, (size_t)(out_features * in_features * 2)) != hipSuccess ||
+      hipMalloc(&p->g, (size_t)(out_features * 4)) != hipSuccess ||
+      hipMalloc(&p->zeros, 256) != hipSuccess)
+    return fail(DSPARK_E_NOMEM);
+  bool ok = hipMemcpy2DAsync(plain, (size_t)(in_features * 2), weight, (size_t)(w_row_stride * 2),
+                             (size_t)(in_features * 2), (size_t)out_features,
+                             hipMemcpyDeviceToDevice, stream) == hipSuccess;
+  ok = ok && dspark::launch_block_weight(plain, out_features, in_features, p->w, stream) ==
+                 hipSuccess;
+  ok = ok && dspark::launch_widen_to_f32(norm_weight, norm_weight_dtype, p->g, out_features,
+                                         stream) == hipSuccess;
+  ok = ok && hipMemsetAsync(p->zeros, 0, 256, stream) == hipSuccess;
+  ok = ok && hipStreamSynchronize(stream) == hipSuccess;
+  if (!ok) return fail(DSPARK_E_DEVICE);
+  (void)hipFree(plain);
+  *out = p;
+  return DSPARK_OK;
+}
+
+int dspark_main_proj_workspace_bytes(const dspark_main_proj_pack* p, int64_t num_tokens,
+                                     int64_t* bytes) {
+  if (!p || !bytes || num_tokens < 0) return DSPARK_E_INVALID;
+  *bytes = (p->out_features / 128) * num_tokens * (int64_t)sizeof(float);
+  return DSPARK_OK;
+}
+
+int dspark_main_proj_norm(const dspark_main_proj_pack* p, const void* aux_hidden,
+                          int64_t num_tokens, int64_t aux_row_stride, void* ctx_hidden,
+                          int64_t ctx_row_stride, void* workspace, int64_t workspace_bytes,
+                          void* stream_ptr) {
+  if (!p || num_tokens < 0) return DSPARK_E_INVALID;
+  if (num_tokens == 0) return DSPARK_OK;
+  if (!aux_hidden || !ctx_hidden || !workspace) return DSPARK_E_INVALID;
+  if (aux_row_stride < p->in_features || aux_row_stride % 8 != 0 ||
+      ctx_row_stride < p->out_features || ctx_row_stride % 8 != 0 ||
+      reinterpret_cast<uintptr_t>(aux_hidden) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(ctx_hidden) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return DSPARK_E_INVALID;
+  const int64_t groups = p->out_features / 128;
+  if (workspace_bytes < groups * num_tokens * (int64_t)sizeof(float)) return DSPARK_E_INVALID;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return DSPARK_E_DEVICE;
+  if (dev != p->device) return DSPARK_E_INVALID;
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  dspark::WriteArgs a = {};
+  a.x = static_cast<const uint16_t*>(aux_hidden);
+  a.w = p->w;
+  a.zeros = p->zeros;
+  a.x_stride = aux_row_stride;
+  a.T = num_tokens;
+  a.H = (int32_t)p->in_features;
+  a.R = groups;
+  a.y = static_cast<uint16_t*>(ctx_hidden);
+  a.y_stride = ctx_row_stride;
+  a.partial = static_cast<float*>(workspace);
+  const bool fp16 = p->dtype == DSPARK_FP16;
+  if (dspark::launch_rows_out(a, fp16, p->num_cus, stream) != hipSuccess) return DSPARK_E_DEVICE;
+  if (dspark::launch_row_norm(a.y, ctx_row_stride, a.partial, num_tokens, groups, p->g, p->eps,
+                              fp16, stream) != hipSuccess)
+    return DSPARK_E_DEVICE;
+  return DSPARK_OK;
+}
+
+void dspark_main_proj_free(dspark_main_proj_pack* p) { free_proj(p); }

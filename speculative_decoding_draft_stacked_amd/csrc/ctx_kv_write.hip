@@ -175,6 +175,44 @@ __device__ __forceinline__ void scatter_tile(const WriteArgs& a, const uint16_t*
   }
 }
 
+// Head dimension value that selects the context producer's epilogue instead
+// of the K/V scatter: the tile's rows are plain output features.
+constexpr int kRowsOut = 0;
+
+// Producer epilogue: from the dtype-rounded LDS tile [BT][LDO] (tokens x ROWS
+// output features), store each token's features to its output row and write
+// the sum of squares of every 128-feature group (in fp32, of the rounded
+// values) to partial[group * T + token] for the row norm that follows. 16
+// lanes per (token, group), 8 features each.
+template <typename E, int BT, int LDO, int NT, int ROWS>
+__device__ __forceinline__ void rows_out_tile(const WriteArgs& a, const uint16_t* sO, int64_t n0,
+                                              int64_t t0, int tid) {
+  constexpr int GROUPS = ROWS / BN;
+  constexpr int LPG = BN / 8;
+  constexpr int TASK_LANES = BT * GROUPS * LPG;
+  static_assert(NT % 64 == 0 && TASK_LANES % LPG == 0, "lane groups stay inside a wave");
+#pragma unroll 1
+  for (int idx = tid; idx < TASK_LANES; idx += NT) {
+    const int task = idx / LPG;
+    const int j = idx % LPG;
+    const int tt = task / GROUPS;
+    const int g = task % GROUPS;
+    const int64_t t = t0 + tt;
+    const int64_t rt = n0 / BN + g;
+    if (t >= a.T || rt >= a.R) continue;  // uniform over the LPG lanes of a task
+    const uint4 u = *reinterpret_cast<const uint4*>(sO + tt * LDO + g * BN + j * 8);
+    float f[8];
+    unpack8<E>(u, f);
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += f[i] * f[i];
+#pragma unroll
+    for (int m = 1; m < LPG; m <<= 1) ss += __shfl_xor(ss, m);
+    *reinterpret_cast<uint4*>(a.y + t * a.y_stride + rt * BN + j * 8) = u;
+    if (j == 0) a.partial[rt * a.T + t] = ss;
+  }
+}
+
 // 16-byte direct-to-LDS load (gfx950 global_load_lds_dwordx4): lane i of the
 // wave writes its 16 bytes to lds_wave_base + 16 * i; lds_wave_base must be
 // the same for the whole wave.
@@ -263,7 +301,7 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
   // and each XCD (workgroup b runs on XCD b % 8) takes a contiguous run of
   // that order, so the workgroups resident on one XCD share weight and token
   // tiles through its L2.
-  const int64_t R = (int64_t)a.L * 2 * a.NH * D / BN;  // 128-row weight tiles
+  const int64_t R = a.R;  // 128-row weight tiles
   const int64_t RP = (R + 1) / 2;                       // 256-row tiles
   const int64_t ntiles = RP * t_tiles;
   const int64_t b = blockIdx.x;
@@ -398,7 +436,10 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
     }
   }
   __syncthreads();
-  scatter_tile<E, D, BT, COMMIT, LDO, NT, ROWS>(a, sO, n0, t0, tid);
+  if constexpr (D == kRowsOut)
+    rows_out_tile<E, BT, LDO, NT, ROWS>(a, sO, n0, t0, tid);
+  else
+    scatter_tile<E, D, BT, COMMIT, LDO, NT, ROWS>(a, sO, n0, t0, tid);
 }
 
 // Weight-streaming kernel for small T (decode-sized batches). A workgroup
@@ -443,7 +484,7 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
   const int hh = lane >> 5;
   const int64_t T = a.T;
   const int H = a.H;
-  const int64_t R = (int64_t)a.L * 2 * a.NH * D / BN;
+  const int64_t R = a.R;
   // Workgroup b runs on XCD b % 8. When the row tiles divide evenly, the
   // `splits` workgroups sharing a weight tile are placed on one XCD and
   // dispatched back to back, so its L2 serves the tile to all of them.
@@ -566,7 +607,10 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
     }
   }
   __syncthreads();
-  scatter_tile<E, D, BT, COMMIT, LDO, NT>(a, sO, n0, t0, tid);
+  if constexpr (D == kRowsOut)
+    rows_out_tile<E, BT, LDO, NT, BN>(a, sO, n0, t0, tid);
+  else
+    scatter_tile<E, D, BT, COMMIT, LDO, NT>(a, sO, n0, t0, tid);
 }
 
 template <bool FP16, int D, bool BIAS, bool COMMIT, int BT>
@@ -582,8 +626,7 @@ hipError_t launch_tiled_bt(const WriteArgs& a, int64_t grid, int64_t t_tiles, hi
 // the larger tile, which needs fewer line requests per MFMA.
 template <bool FP16, int D, bool BIAS, bool COMMIT>
 hipError_t launch_tiled(const WriteArgs& a, int num_cus, hipStream_t stream) {
-  const int64_t r_tiles = (int64_t)a.L * 2 * a.NH * D / BN;
-  const int64_t rp = (r_tiles + 1) / 2;
+  const int64_t rp = (a.R + 1) / 2;
   int best_bt = 256;
   int64_t best_cost = -1;
   for (int bt : {256, 192, 128}) {
@@ -612,7 +655,7 @@ hipError_t launch_stream_nb(const WriteArgs& a, int64_t row_tiles, int splits, h
 // to 4 blocks of 32 tokens) fits on the device. Larger T: LDS-tiled kernel.
 template <bool FP16, int D, bool BIAS, bool COMMIT>
 hipError_t launch_by_rows(const WriteArgs& a, int num_cus, hipStream_t stream) {
-  const int64_t row_tiles = (int64_t)a.L * 2 * a.NH * D / BN;
+  const int64_t row_tiles = a.R;
   const int64_t blocks = (a.T + 31) / 32;
   const int64_t cap = row_tiles >= num_cus ? 1 : num_cus / row_tiles;
   if (blocks > 4 * cap) return launch_tiled<FP16, D, BIAS, COMMIT>(a, num_cus, stream);
@@ -649,6 +692,12 @@ hipError_t launch_dim(const WriteArgs& a, int head_dim, bool has_bias, bool has_
 }
 
 }  // namespace
+
+hipError_t launch_rows_out(const WriteArgs& a, bool is_fp16, int num_cus, hipStream_t stream) {
+  if (num_cus < 1) num_cus = 1;
+  return is_fp16 ? launch_by_rows<true, kRowsOut, false, false>(a, num_cus, stream)
+                 : launch_by_rows<false, kRowsOut, false, false>(a, num_cus, stream);
+}
 
 hipError_t launch_ctx_kv_write(const WriteArgs& a, int head_dim, bool is_fp16, bool has_bias,
                                bool has_commit, int num_cus, hipStream_t stream) {

@@ -23,6 +23,10 @@ struct WriteArgs {
   const int64_t* locs;      // [T]
   const int64_t* commit;    // [T / W] or nullptr
   unsigned long long* err;  // range error counter
+  uint16_t* y;              // producer only: [T, R * 128] output rows (row stride y_stride)
+  float* partial;           // producer only: [R, T] sums of squares per 128-feature group
+  int64_t y_stride;
+  int64_t R;                // 128-row tiles of the blocked weight
   int64_t x_stride;
   int64_t T;
   int64_t P;
@@ -75,6 +79,16 @@ struct VerifyArgs {
 // Launches the verify accept/bonus kernel for `a` on `stream` (validated by
 // the caller). Returns the launch status.
 hipError_t launch_verify_accept(const VerifyArgs& a, hipStream_t stream);
+
+// Launches the context producer's GEMM for `a` (x = aux hidden, w = blocked
+// projection weight with a.R row tiles, H = input features): rounded outputs
+// to a.y and per-(128-feature group, token) sums of squares to a.partial.
+hipError_t launch_rows_out(const WriteArgs& a, bool is_fp16, int num_cus, hipStream_t stream);
+
+// Launches the row RMSNorm that completes the producer, in place on y.
+hipError_t launch_row_norm(uint16_t* y, int64_t y_stride, const float* partial, int64_t T,
+                           int64_t groups, const float* g, float eps, bool is_fp16,
+                           hipStream_t stream);
 
 // Launches the fused GEMM + norm + rotation + scatter for `a` on `stream`.
 // `num_cus` (compute units of the device) sizes the small-T grid. Shapes have

@@ -199,3 +199,41 @@ def test_verify_empty_is_ok():
 ])
 def test_verify_invalid_arguments(kw):
     assert _verify(**kw) == dk.E_INVALID
+
+
+# ------------------------------------------------------------ context producer
+
+def _proj_pack(out_f=256, in_f=768, stride=768, wdt=dk.BF16, gdt=dk.BF16, eps=1e-6,
+               act=dk.BF16, w=16, g=16):
+    """Host-side checks only: fake non-NULL pointers are never dereferenced
+    before a check fails."""
+    h = ctypes.c_void_p(0)
+    r = ctypes.c_int32(-7)
+    st = dk.lib().dspark_pack_main_proj(w, out_f, in_f, stride, wdt, g, gdt, eps, act, None,
+                                        ctypes.byref(h), ctypes.byref(r))
+    return st, r.value, h.value
+
+
+@pytest.mark.parametrize("kw,reason", [
+    (dict(act=dk.FP32, wdt=dk.FP32), 7), (dict(wdt=dk.FP16), 3), (dict(gdt=dk.FP16), 7),
+    (dict(out_f=200), 6), (dict(in_f=770, stride=776), 6), (dict(stride=772), 6), (dict(w=24), 6),
+])
+def test_proj_pack_fallbacks(kw, reason):
+    st, r, h = _proj_pack(**kw)
+    assert (st, r, h) == (dk.FALLBACK, reason, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(w=None), dict(g=None), dict(out_f=0), dict(in_f=-8), dict(stride=760),
+    dict(eps=-1.0), dict(eps=float("nan")),
+])
+def test_proj_pack_invalid(kw):
+    assert _proj_pack(**kw)[0] == dk.E_INVALID
+
+
+def test_proj_calls_reject_null_pack():
+    n = ctypes.c_int64(5)
+    lib = dk.lib()
+    assert lib.dspark_main_proj_workspace_bytes(None, 4, ctypes.byref(n)) == dk.E_INVALID
+    assert lib.dspark_main_proj_norm(None, 16, 4, 768, 16, 256, 16, 1 << 20, None) == dk.E_INVALID
+    lib.dspark_main_proj_free(None)  # no-op
