@@ -477,10 +477,21 @@ int dspark_pack_main_proj(const void* weight, int64_t out_features, int64_t in_f
   return DSPARK_OK;
 }
 
+namespace {
+// Workspace of one producer call: fp32 partial projections when the
+// projection is split over K, else one fp32 sum of squares per 128-feature
+// group and token.
+int64_t proj_workspace_bytes(const dspark_main_proj_pack* p, int64_t T) {
+  const int64_t groups = p->out_features / 128;
+  const int ks = dspark::producer_ksplits(T, groups, p->in_features, p->out_features, p->num_cus);
+  return (ks > 1 ? ks * p->out_features : groups) * T * (int64_t)sizeof(float);
+}
+}  // namespace
+
 int dspark_main_proj_workspace_bytes(const dspark_main_proj_pack* p, int64_t num_tokens,
                                      int64_t* bytes) {
   if (!p || !bytes || num_tokens < 0) return DSPARK_E_INVALID;
-  *bytes = (p->out_features / 128) * num_tokens * (int64_t)sizeof(float);
+  *bytes = proj_workspace_bytes(p, num_tokens);
   return DSPARK_OK;
 }
 
@@ -498,7 +509,9 @@ int dspark_main_proj_norm(const dspark_main_proj_pack* p, const void* aux_hidden
       reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
     return DSPARK_E_INVALID;
   const int64_t groups = p->out_features / 128;
-  if (workspace_bytes < groups * num_tokens * (int64_t)sizeof(float)) return DSPARK_E_INVALID;
+  if (workspace_bytes < proj_workspace_bytes(p, num_tokens)) return DSPARK_E_INVALID;
+  const int ks = dspark::producer_ksplits(num_tokens, groups, p->in_features, p->out_features,
+                                          p->num_cus);
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return DSPARK_E_DEVICE;
   if (dev != p->device) return DSPARK_E_INVALID;
@@ -514,10 +527,11 @@ int dspark_main_proj_norm(const dspark_main_proj_pack* p, const void* aux_hidden
   a.y = static_cast<uint16_t*>(ctx_hidden);
   a.y_stride = ctx_row_stride;
   a.partial = static_cast<float*>(workspace);
+  a.ksplits = ks;
   const bool fp16 = p->dtype == DSPARK_FP16;
   if (dspark::launch_rows_out(a, fp16, p->num_cus, stream) != hipSuccess) return DSPARK_E_DEVICE;
-  if (dspark::launch_row_norm(a.y, ctx_row_stride, a.partial, num_tokens, groups, p->g, p->eps,
-                              fp16, stream) != hipSuccess)
+  if (dspark::launch_row_norm(a.y, ctx_row_stride, a.partial, num_tokens, groups, ks, p->g,
+                              p->eps, fp16, stream) != hipSuccess)
     return DSPARK_E_DEVICE;
   return DSPARK_OK;
 }

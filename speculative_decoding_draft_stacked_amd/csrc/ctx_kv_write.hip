@@ -488,7 +488,12 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
   // Workgroup b runs on XCD b % 8. When the row tiles divide evenly, the
   // `splits` workgroups sharing a weight tile are placed on one XCD and
   // dispatched back to back, so its L2 serves the tile to all of them.
-  const int64_t b = blockIdx.x;
+  // The producer may also split K over workgroups (a.ksplits > 1): workgroup
+  // b takes K part b / (R * splits) and writes fp32 partial sums instead of
+  // the epilogue; the row-norm kernel adds the parts.
+  const int ks = (D == kRowsOut && a.ksplits > 1) ? a.ksplits : 1;
+  const int64_t kq = (int64_t)blockIdx.x / (R * splits);
+  const int64_t b = (int64_t)blockIdx.x % (R * splits);
   int64_t rt, sp;
   if (R % 8 == 0) {
     const int64_t i = b / 8;
@@ -500,12 +505,14 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
   }
   const int64_t n0 = rt * BN;
   const int64_t t0 = sp * BT;
-  const int nk = (H + BK - 1) / BK;
+  const int nk_all = (H + BK - 1) / BK;
+  const int kc0 = (int)(kq * nk_all / ks);         // this part's chunks [kc0, kc1)
+  const int nk = (int)((kq + 1) * nk_all / ks) - kc0;
   const int ng = (nk + 1) / 2;
   const int ng_ring = (ng + SLOTS - 1) / SLOTS * SLOTS;
 
   // this wave's pieces of weight block (rt, c): one contiguous KiB per MFMA step
-  const uint16_t* wblk = a.w + rt * nk * 8192 + (w * 4 * 64 + lane) * 8;
+  const uint16_t* wblk = a.w + (rt * nk_all + kc0) * 8192 + (w * 4 * 64 + lane) * 8;
   // X direct loads: instruction i of wave (w, par) fills LDS slots
   // [256 i + 64 w, +64) of its chunk's stage; slot s holds piece
   // (s % 8) ^ ((t / 2) % 8) of token t = s / 8. Per-lane source offsets are
@@ -524,14 +531,14 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
 
   uint4 wq[SLOTS][4];
   auto issue = [&](int g, uint4(&wd)[4]) {
-    const int c = 2 * g + par;
-    const bool live = c < nk;  // chunks past the end read the zero page
+    const int c = 2 * g + par;  // chunk of this part (the stage follows it)
+    const bool live = c < nk;   // chunks past the end read the zero page
     const uint16_t* wsrc = live ? wblk + (int64_t)c * 8192 : a.zeros;
     const int wstep = live ? 512 : 0;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) wd[kk] = ldg16(wsrc + kk * wstep);
     uint16_t* stage = smem + ((c % XSTAGES) * SXE);
-    const int kbase = c * BK;
+    const int kbase = (kc0 + c) * BK;
 #pragma unroll
     for (int i = 0; i < XPW; ++i) {
       const bool ok = live && kbase + xcol[i] < H;
@@ -585,6 +592,25 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
       }
   }
   __syncthreads();
+  if (D == kRowsOut && ks > 1) {
+    // fp32 partial sums of this K part: partial[(kq * T + t) * (R * 128) + n]
+    if (par == 0) {
+#pragma unroll
+      for (int tb = 0; tb < NB; ++tb) {
+        const int tok = tb * 32 + r32;
+        if (t0 + tok >= T) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = 32 * w + 8 * q + 4 * hh;
+          const float4 o = *reinterpret_cast<const float4*>(red + tok * RS + row);
+          *reinterpret_cast<float4*>(a.partial + (kq * T + t0 + tok) * (R * BN) + n0 + row) =
+              make_float4(acc[tb][4 * q] + o.x, acc[tb][4 * q + 1] + o.y,
+                          acc[tb][4 * q + 2] + o.z, acc[tb][4 * q + 3] + o.w);
+        }
+      }
+    }
+    return;
+  }
   if (par == 0) {
 #pragma unroll
     for (int tb = 0; tb < NB; ++tb) {
@@ -695,8 +721,38 @@ hipError_t launch_dim(const WriteArgs& a, int head_dim, bool has_bias, bool has_
 
 hipError_t launch_rows_out(const WriteArgs& a, bool is_fp16, int num_cus, hipStream_t stream) {
   if (num_cus < 1) num_cus = 1;
+  if (a.ksplits > 1) {  // 128-token tiles x K parts (see producer_plan)
+    const int64_t splits = (a.T + 127) / 128;
+    const int64_t grid = a.R * splits * a.ksplits;
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (is_fp16)
+      hipLaunchKernelGGL((ctx_kv_stream_kernel<true, kRowsOut, false, false, 4>), dim3((uint32_t)grid),
+                         dim3(512), 0, stream, a, (int)splits);
+    else
+      hipLaunchKernelGGL((ctx_kv_stream_kernel<false, kRowsOut, false, false, 4>),
+                         dim3((uint32_t)grid), dim3(512), 0, stream, a, (int)splits);
+    return hipGetLastError();
+  }
   return is_fp16 ? launch_by_rows<true, kRowsOut, false, false>(a, num_cus, stream)
                  : launch_by_rows<false, kRowsOut, false, false>(a, num_cus, stream);
+}
+
+int producer_ksplits(int64_t T, int64_t R, int64_t in_features, int64_t out_features,
+                     int num_cus) {
+  // Split K only where the write kernels' small-T path would run (so that the
+  // grid is one round) and 128-token tiles alone leave the device
+  // under-filled; the row norm then holds a row in registers (<= 8192).
+  if (num_cus < 1) num_cus = 1;
+  const int64_t cap = R >= num_cus ? 1 : num_cus / R;
+  const int64_t blocks32 = (T + 31) / 32;
+  if (blocks32 > 4 * cap || out_features > 8192) return 1;
+  const int64_t tiles = R * ((T + 127) / 128);
+  if (tiles >= num_cus) return 1;
+  int64_t ks = num_cus / tiles;
+  const int64_t nk = (in_features + 63) / 64;
+  if (ks > nk / 8) ks = nk / 8;  // at least 8 chunks of 64 per part
+  if (ks > 16) ks = 16;
+  return ks < 2 ? 1 : (int)ks;
 }
 
 hipError_t launch_ctx_kv_write(const WriteArgs& a, int head_dim, bool is_fp16, bool has_bias,

@@ -27,6 +27,7 @@ struct WriteArgs {
   float* partial;           // producer only: [R, T] sums of squares per 128-feature group
   int64_t y_stride;
   int64_t R;                // 128-row tiles of the blocked weight
+  int32_t ksplits;          // producer only: K parts over workgroups (<= 1: none)
   int64_t x_stride;
   int64_t T;
   int64_t P;
@@ -85,9 +86,16 @@ hipError_t launch_verify_accept(const VerifyArgs& a, hipStream_t stream);
 // to a.y and per-(128-feature group, token) sums of squares to a.partial.
 hipError_t launch_rows_out(const WriteArgs& a, bool is_fp16, int num_cus, hipStream_t stream);
 
-// Launches the row RMSNorm that completes the producer, in place on y.
+// K parts the producer's projection is split into for these sizes (1: none).
+int producer_ksplits(int64_t T, int64_t R, int64_t in_features, int64_t out_features,
+                     int num_cus);
+
+// Launches the row RMSNorm that completes the producer. With ksplits <= 1, y
+// holds the rounded projection and `partial` the [groups, T] group sums of
+// squares; with ksplits > 1, `partial` holds [ksplits, T, groups * 128] fp32
+// partial projections and y is written whole.
 hipError_t launch_row_norm(uint16_t* y, int64_t y_stride, const float* partial, int64_t T,
-                           int64_t groups, const float* g, float eps, bool is_fp16,
+                           int64_t groups, int ksplits, const float* g, float eps, bool is_fp16,
                            hipStream_t stream);
 
 // Launches the fused GEMM + norm + rotation + scatter for `a` on `stream`.

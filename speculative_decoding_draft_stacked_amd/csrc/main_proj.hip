@@ -10,10 +10,13 @@
 // inv = 1 / sqrt(sum / H + eps) and rewrites the row in place as
 // round(y * inv * g), in fp32 with the weight widened to fp32 at pack time.
 //
+// When the projection is split over K for small batches, its workgroups leave
+// fp32 partial sums instead, and the norm kernel first adds a token's parts in
+// a fixed order and rounds them (the projection's output rounding).
+//
 // Mapping: one wave per token row, 16-byte accesses, 8 features per lane per
-// pass (a pass covers 512 features); the group sums are read by lanes
-// 0..groups-1 and reduced by a butterfly, which leaves the same bits in every
-// lane.
+// pass (a pass covers 512 features); sums across the wave use a butterfly,
+// which leaves the same bits in every lane.
 #include "internal.h"
 
 namespace dspark {
@@ -65,20 +68,91 @@ __global__ __launch_bounds__(kThreads) void row_norm_kernel(uint16_t* y, int64_t
   }
 }
 
+// K-split form: partial holds ksplits fp32 partial projections [ks, T, H].
+// A wave adds its token's parts in order (deterministic), rounds to the dtype
+// (the linear's output rounding), keeps the row in registers (H <= 8192:
+// 16 passes of 512 features), and writes round(y * inv * g).
+constexpr int kMaxPasses = 16;
+
+template <bool FP16>
+__global__ __launch_bounds__(kThreads) void row_norm_split_kernel(uint16_t* y, int64_t y_stride,
+                                                                   const float* partial,
+                                                                   int64_t T, int64_t H, int ks,
+                                                                   const float* g, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (t >= T) return;  // uniform over the wave
+  uint32_t yv[kMaxPasses][4];
+  float ss = 0.0f;
+#pragma unroll
+  for (int pp = 0; pp < kMaxPasses; ++pp) {
+    const int64_t c = (int64_t)pp * 512 + lane * 8;
+    if (c < H) {
+      float sum[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+      for (int q = 0; q < ks; ++q) {
+        const float* src = partial + ((int64_t)q * T + t) * H + c;
+        const float4 a0 = *reinterpret_cast<const float4*>(src);
+        const float4 a1 = *reinterpret_cast<const float4*>(src + 4);
+        sum[0] += a0.x, sum[1] += a0.y, sum[2] += a0.z, sum[3] += a0.w;
+        sum[4] += a1.x, sum[5] += a1.y, sum[6] += a1.z, sum[7] += a1.w;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = from_f<FP16>(sum[2 * i]), hi = from_f<FP16>(sum[2 * i + 1]);
+        const float flo = to_f<FP16>(lo), fhi = to_f<FP16>(hi);
+        ss += flo * flo + fhi * fhi;
+        yv[pp][i] = lo | (hi << 16);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+  const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+  uint16_t* row = y + t * y_stride;
+#pragma unroll
+  for (int pp = 0; pp < kMaxPasses; ++pp) {
+    const int64_t c = (int64_t)pp * 512 + lane * 8;
+    if (c < H) {
+      const float4 g0 = *reinterpret_cast<const float4*>(g + c);
+      const float4 g1 = *reinterpret_cast<const float4*>(g + c + 4);
+      const float gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float lo = to_f<FP16>(yv[pp][i] & 0xFFFFu) * inv * gw[2 * i];
+        const float hi = to_f<FP16>(yv[pp][i] >> 16) * inv * gw[2 * i + 1];
+        o[i] = from_f<FP16>(lo) | (from_f<FP16>(hi) << 16);
+      }
+      *reinterpret_cast<uint4*>(row + c) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_row_norm(uint16_t* y, int64_t y_stride, const float* partial, int64_t T,
-                           int64_t groups, const float* g, float eps, bool is_fp16,
+                           int64_t groups, int ksplits, const float* g, float eps, bool is_fp16,
                            hipStream_t stream) {
   if (T <= 0) return hipSuccess;
   const int64_t blocks = (T + kThreads / 64 - 1) / (kThreads / 64);
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (is_fp16)
-    hipLaunchKernelGGL(row_norm_kernel<true>, dim3((uint32_t)blocks), dim3(kThreads), 0, stream,
-                       y, y_stride, partial, T, groups, g, eps);
-  else
-    hipLaunchKernelGGL(row_norm_kernel<false>, dim3((uint32_t)blocks), dim3(kThreads), 0, stream,
-                       y, y_stride, partial, T, groups, g, eps);
+  const dim3 grid((uint32_t)blocks), block(kThreads);
+  if (ksplits > 1) {
+    const int64_t H = groups * 128;
+    if (H > kMaxPasses * 512) return hipErrorInvalidValue;
+    if (is_fp16)
+      hipLaunchKernelGGL(row_norm_split_kernel<true>, grid, block, 0, stream, y, y_stride,
+                         partial, T, H, ksplits, g, eps);
+    else
+      hipLaunchKernelGGL(row_norm_split_kernel<false>, grid, block, 0, stream, y, y_stride,
+                         partial, T, H, ksplits, g, eps);
+  } else if (is_fp16) {
+    hipLaunchKernelGGL(row_norm_kernel<true>, grid, block, 0, stream, y, y_stride, partial, T,
+                       groups, g, eps);
+  } else {
+    hipLaunchKernelGGL(row_norm_kernel<false>, grid, block, 0, stream, y, y_stride, partial, T,
+                       groups, g, eps);
+  }
   return hipGetLastError();
 }
 
