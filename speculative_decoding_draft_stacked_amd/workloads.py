@@ -423,3 +423,77 @@ def proj_workload(name: str) -> ProjCase:
     """The named producer workload with its fixed seed (4000 + its 1-based index)."""
     seed = 4000 + PROJ_WORKLOAD_ORDER.index(name) + 1
     return make_proj_case(name=name, seed=seed, **PROJ_WORKLOADS[name])
+
+
+# ---------------------------------------------------------------------------
+# Inputs of the draft attention over the KV pool (sglang PR #35499, key source
+# snippets: the shared-KV stage-1/stage-2 kernels with KV heads and the causal
+# mask off): per request a block of query tokens, the request's prefix in a
+# layer's pool [slots, NHK, D] listed by slot, and the block's own K/V.
+
+
+@dataclasses.dataclass
+class AttnCase:
+    name: str
+    dtype: str
+    B: int
+    block: int
+    nhq: int
+    nhk: int
+    D: int
+    sm_scale: float
+    slots: int
+    q: np.ndarray           # uint16 [B*block, nhq, D]
+    k_ext: np.ndarray       # uint16 [B*block, nhk, D]
+    v_ext: np.ndarray
+    k_pool: np.ndarray      # uint16 [slots, nhk, D]
+    v_pool: np.ndarray
+    kv_indptr: np.ndarray   # int64 [B+1]
+    kv_indices: np.ndarray  # int64 [kv_indptr[-1]]
+
+    @property
+    def max_prefix(self) -> int:
+        return int(np.max(np.diff(self.kv_indptr))) if self.B else 0
+
+
+def make_attn_case(*, name: str = "attn_case", B: int, block: int, nhq: int, nhk: int, D: int,
+                   prefix, slots: int, dtype: str = BF16, seed: int = 0,
+                   sm_scale: Optional[float] = None, q_std: float = 2.0) -> AttnCase:
+    """Draw one case. Order: q, k_ext, v_ext, k_pool, v_pool, slot permutation.
+    q ~ N(0, q_std) (peaky softmax rows), keys ~ N(0, 1), values ~ N(0.5, 1) (so
+    that outputs are O(1)); requests own disjoint slots, taken in order from
+    one seeded permutation of the pool; ``prefix`` is one length or one per
+    request."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    prefix = np.broadcast_to(np.asarray(prefix, dtype=np.int64), (B,)).copy()
+    if prefix.sum() > slots:
+        raise ValueError("prefixes need more slots than the pool has")
+    T = B * block
+    q = to_bits(rng.standard_normal((T, nhq, D)) * q_std, dtype)
+    k_ext = to_bits(rng.standard_normal((T, nhk, D)), dtype)
+    v_ext = to_bits(rng.standard_normal((T, nhk, D)) + 0.5, dtype)
+    k_pool = to_bits(rng.standard_normal((slots, nhk, D)), dtype)
+    v_pool = to_bits(rng.standard_normal((slots, nhk, D)) + 0.5, dtype)
+    perm = rng.permutation(slots).astype(np.int64)
+    kv_indptr = np.concatenate([[0], np.cumsum(prefix)]).astype(np.int64)
+    kv_indices = perm[:kv_indptr[-1]].copy()
+    return AttnCase(name=name, dtype=dtype, B=B, block=block, nhq=nhq, nhk=nhk, D=D,
+                    sm_scale=1.0 / np.sqrt(D) if sm_scale is None else sm_scale, slots=slots,
+                    q=q, k_ext=k_ext, v_ext=v_ext, k_pool=k_pool, v_pool=v_pool,
+                    kv_indptr=kv_indptr, kv_indices=kv_indices)
+
+
+# Draft-attention workloads: the write's Qwen3-8B-like layer (32 query heads,
+# 8 KV heads of 128) with 32 requests x blocks of 8 over 8k-token prefixes,
+# and a head_dim-64 layer (16 query heads, 4 KV heads) over 16k-token prefixes.
+ATTN_WORKLOADS = {
+    "attn_decode_8k": dict(B=32, block=8, nhq=32, nhk=8, D=128, prefix=8192, slots=32 * 8192),
+    "attn_d64_16k": dict(B=8, block=8, nhq=16, nhk=4, D=64, prefix=16384, slots=8 * 16384),
+}
+ATTN_WORKLOAD_ORDER = ["attn_decode_8k", "attn_d64_16k"]
+
+
+def attn_workload(name: str) -> AttnCase:
+    """The named draft-attention workload with its fixed seed (5000 + index)."""
+    seed = 5000 + ATTN_WORKLOAD_ORDER.index(name) + 1
+    return make_attn_case(name=name, seed=seed, **ATTN_WORKLOADS[name])
