@@ -278,6 +278,62 @@ int dspark_main_proj_norm(const dspark_main_proj_pack* pack, const void* aux_hid
 /* Frees the producer pack (waits for the device first). NULL is a no-op. */
 void dspark_main_proj_free(dspark_main_proj_pack* pack);
 
+/* ------------------------------------------------------------ draft attention
+ * Bidirectional grouped-query attention of the draft over a layer's KV pool
+ * (sglang PR #35499, implementation breakdown and key source snippets: the
+ * shared-KV split-KV stage and the combine stage, query head h reading KV
+ * head h // (num_q_heads / num_kv_heads), the causal mask off for the draft).
+ * Every request b has `block` query tokens (rows b * block + j); its keys and
+ * values are its prefix, the pool slots kv_indices[kv_indptr[b] ..
+ * kv_indptr[b + 1]), followed by the block's own rows of k_ext / v_ext; every
+ * query sees every key of its request:
+ *   o = softmax(q . K^T * sm_scale) V, fp32 accumulation and softmax, the
+ *   probabilities rounded to the dtype for the value product, o rounded once.
+ * All tensors are device memory in the activation dtype with element strides;
+ * the last (head_dim) stride is 1 and rows are 16-byte aligned. */
+typedef struct {
+  const void* q;            /* [num_requests * block, num_q_heads, head_dim] */
+  int64_t q_token_stride, q_head_stride;
+  const void* k_ext;        /* [num_requests * block, num_kv_heads, head_dim] */
+  const void* v_ext;        /* same layout as k_ext */
+  int64_t ext_token_stride, ext_head_stride;
+  const void* k_pool;       /* [num_slots, num_kv_heads, head_dim] */
+  const void* v_pool;       /* same layout as k_pool */
+  int64_t pool_slot_stride, pool_head_stride;
+  int64_t num_slots;
+  const int64_t* kv_indptr;   /* device [num_requests + 1], non-decreasing */
+  const int64_t* kv_indices;  /* device, the prefix slots */
+  void* out;                /* [num_requests * block, num_q_heads, head_dim], written */
+  int64_t out_token_stride, out_head_stride;
+} dspark_attn_desc;
+
+/* Device workspace bytes of dspark_draft_attention for these sizes (one fp32
+ * record of 32 rows x (head_dim + 2) per request, KV head, 32-row tile and
+ * key split). Host-only. Returns DSPARK_OK or DSPARK_E_INVALID. */
+int dspark_draft_attention_workspace_bytes(int64_t num_requests, int32_t block,
+                                           int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int64_t max_prefix, int64_t* bytes);
+
+/* The attention. max_prefix (host) must be >= every request's prefix length:
+ * it sizes the key splits; keys of a prefix past max_prefix are not attended,
+ * and each such request is counted in range_errors. A slot outside [0, num_slots) is skipped and
+ * counted. range_errors: device counter or NULL (atomically added, never
+ * cleared). workspace: device, 16-byte aligned, at least
+ * dspark_draft_attention_workspace_bytes (scratch; calls sharing it on
+ * different streams race). Two launches on `stream`; allocates nothing and
+ * does not synchronise. num_requests == 0 returns DSPARK_OK, nothing enqueued.
+ * Returns DSPARK_OK; DSPARK_FALLBACK with *fallback_reason (may be NULL) =
+ * DSPARK_FB_SHAPE (head_dim not 64 or 128) or DSPARK_FB_DTYPE (not bf16/fp16);
+ * DSPARK_E_INVALID (NULL desc or pointers with work to do, num_q_heads not a
+ * multiple of num_kv_heads, block < 1, strides not multiples of 8 or
+ * misaligned bases, num_slots < 1, workspace too small); DSPARK_E_DEVICE. */
+int dspark_draft_attention(const dspark_attn_desc* desc, int64_t num_requests, int32_t block,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t act_dtype, double sm_scale, int64_t max_prefix,
+                           void* workspace, int64_t workspace_bytes,
+                           unsigned long long* range_errors, void* stream,
+                           int32_t* fallback_reason);
+
 /* Reads and clears the pack's count of rows skipped for an out-of-range
  * position or slot. Synchronises `stream`. Returns DSPARK_OK or an error. */
 int dspark_pack_range_errors(const dspark_ctx_kv_pack* pack, void* stream, int64_t* count);

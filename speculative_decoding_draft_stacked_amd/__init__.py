@@ -33,7 +33,8 @@ EXPORTS = [
     "dspark_pack_range_errors", "dspark_pack_info", "dspark_pack_buffers", "dspark_pack_free",
     "dspark_status_str", "dspark_fallback_str", "dspark_table_qk_norm_rope",
     "dspark_verify_accept", "dspark_pack_main_proj", "dspark_main_proj_workspace_bytes",
-    "dspark_main_proj_norm", "dspark_main_proj_free",
+    "dspark_main_proj_norm", "dspark_main_proj_free", "dspark_draft_attention_workspace_bytes",
+    "dspark_draft_attention",
 ]
 
 
@@ -79,6 +80,30 @@ class PoolDesc(ctypes.Structure):
     ]
 
 
+class AttnDesc(ctypes.Structure):
+    """Mirror of dspark_attn_desc."""
+
+    _fields_ = [
+        ("q", ctypes.c_void_p),
+        ("q_token_stride", ctypes.c_int64),
+        ("q_head_stride", ctypes.c_int64),
+        ("k_ext", ctypes.c_void_p),
+        ("v_ext", ctypes.c_void_p),
+        ("ext_token_stride", ctypes.c_int64),
+        ("ext_head_stride", ctypes.c_int64),
+        ("k_pool", ctypes.c_void_p),
+        ("v_pool", ctypes.c_void_p),
+        ("pool_slot_stride", ctypes.c_int64),
+        ("pool_head_stride", ctypes.c_int64),
+        ("num_slots", ctypes.c_int64),
+        ("kv_indptr", ctypes.c_void_p),
+        ("kv_indices", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("out_token_stride", ctypes.c_int64),
+        ("out_head_stride", ctypes.c_int64),
+    ]
+
+
 _lib = None
 
 
@@ -109,6 +134,9 @@ def lib() -> ctypes.CDLL:
                                             i32, vp, ctypes.POINTER(vp), p_i32]
         L.dspark_main_proj_workspace_bytes.argtypes = [vp, i64, p_i64]
         L.dspark_main_proj_norm.argtypes = [vp, vp, i64, i64, vp, i64, vp, i64, vp]
+        L.dspark_draft_attention_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, i64, p_i64]
+        L.dspark_draft_attention.argtypes = [ctypes.POINTER(AttnDesc), i64, i32, i32, i32, i32,
+                                             i32, ctypes.c_double, i64, vp, i64, vp, vp, p_i32]
         L.dspark_main_proj_free.argtypes = [vp]
         L.dspark_main_proj_free.restype = None
         L.dspark_pack_free.argtypes = [vp]
@@ -121,7 +149,8 @@ def lib() -> ctypes.CDLL:
                      "dspark_pack_range_errors", "dspark_pack_info", "dspark_pack_buffers",
                      "dspark_table_qk_norm_rope", "dspark_verify_accept",
                      "dspark_pack_main_proj", "dspark_main_proj_workspace_bytes",
-                     "dspark_main_proj_norm"):
+                     "dspark_main_proj_norm", "dspark_draft_attention_workspace_bytes",
+                     "dspark_draft_attention"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -426,3 +455,47 @@ def main_proj_norm(pack: ProjPack, aux_hidden, ctx_hidden, workspace, stream=Non
                                      workspace.numel() * workspace.element_size(),
                                      _stream(stream))
     _raise_for(st, "dspark_main_proj_norm")
+
+
+def draft_attention_workspace_bytes(num_requests: int, block: int, num_q_heads: int,
+                                    num_kv_heads: int, head_dim: int, max_prefix: int) -> int:
+    n = ctypes.c_int64(0)
+    _raise_for(lib().dspark_draft_attention_workspace_bytes(num_requests, block, num_q_heads,
+                                                            num_kv_heads, head_dim, max_prefix,
+                                                            ctypes.byref(n)),
+               "dspark_draft_attention_workspace_bytes")
+    return n.value
+
+
+def draft_attention(q, k_ext, v_ext, k_pool, v_pool, kv_indptr, kv_indices, out, block: int,
+                    sm_scale: float, max_prefix: int, workspace, range_errors=None,
+                    stream=None) -> bool:
+    """Enqueue the draft attention: q / out [B*block, NHQ, D], k_ext / v_ext
+    [B*block, NHK, D], pools [slots, NHK, D] (unit head-dim stride, same layout
+    for K and V), int64 kv_indptr [B+1] and kv_indices. True when enqueued,
+    False on fallback; ValueError on misuse."""
+    for t in (q, k_ext, v_ext, k_pool, v_pool, out):
+        if t.dim() != 3 or t.stride(2) != 1:
+            raise ValueError("attention tensors are [rows, heads, head_dim], unit last stride")
+    if k_ext.stride() != v_ext.stride() or k_pool.stride() != v_pool.stride():
+        raise ValueError("K and V must share a layout")
+    B = kv_indptr.numel() - 1
+    desc = AttnDesc(q=q.data_ptr(), q_token_stride=q.stride(0), q_head_stride=q.stride(1),
+                    k_ext=k_ext.data_ptr(), v_ext=v_ext.data_ptr(),
+                    ext_token_stride=k_ext.stride(0), ext_head_stride=k_ext.stride(1),
+                    k_pool=k_pool.data_ptr(), v_pool=v_pool.data_ptr(),
+                    pool_slot_stride=k_pool.stride(0), pool_head_stride=k_pool.stride(1),
+                    num_slots=k_pool.shape[0], kv_indptr=kv_indptr.data_ptr(),
+                    kv_indices=kv_indices.data_ptr(), out=out.data_ptr(),
+                    out_token_stride=out.stride(0), out_head_stride=out.stride(1))
+    reason = ctypes.c_int32(0)
+    st = lib().dspark_draft_attention(ctypes.byref(desc), B, block, q.shape[1], k_ext.shape[1],
+                                      q.shape[2], _dtype_code(q), sm_scale, max_prefix,
+                                      workspace.data_ptr(),
+                                      workspace.numel() * workspace.element_size(),
+                                      None if range_errors is None else range_errors.data_ptr(),
+                                      _stream(stream), ctypes.byref(reason))
+    if st == FALLBACK:
+        return False
+    _raise_for(st, "dspark_draft_attention")
+    return True

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdspark.so")
 SOURCES = ["api.hip", "pack_kernels.hip", "ctx_kv_write.hip", "qk_norm_rope.hip", "verify_accept.hip",
-           "main_proj.hip"]
+           "main_proj.hip", "draft_attention.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -537,3 +537,127 @@ int dspark_main_proj_norm(const dspark_main_proj_pack* p, const void* aux_hidden
 }
 
 void dspark_main_proj_free(dspark_main_proj_pack* p) { free_proj(p); }
+
+// ------------------------------------------------------------ draft attention
+
+namespace {
+// Compute units of the current device, queried once per device.
+int current_device_cus() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) cached[dev] = n;
+  return n;
+}
+
+struct AttnPlan {
+  int32_t row_tiles = 0;
+  int32_t n_splits = 0;
+  int64_t split_len = 32;
+  int64_t bytes = 0;
+};
+
+// Key splits: enough waves for about 8 per compute unit, each split a
+// multiple of 32 keys and at least 256 (fewer, longer splits when the batch
+// alone fills the device).
+AttnPlan attn_plan(int64_t B, int32_t block, int32_t nhq, int32_t nhk, int32_t D,
+                   int64_t max_prefix, int num_cus) {
+  AttnPlan pl;
+  const int64_t M = (int64_t)block * (nhq / nhk);
+  pl.row_tiles = (int32_t)((M + 31) / 32);
+  const int64_t base = B * nhk * pl.row_tiles;
+  if (max_prefix > 0) {
+    const int64_t target = 8LL * (num_cus > 0 ? num_cus : 1);
+    int64_t ns = base > 0 ? (target + base - 1) / base : 1;
+    if (ns < 1) ns = 1;
+    int64_t len = (max_prefix + ns - 1) / ns;
+    len = (len + 31) / 32 * 32;
+    if (len < 256) len = 256;
+    pl.split_len = len;
+    pl.n_splits = (int32_t)((max_prefix + len - 1) / len);
+  }
+  pl.bytes = base * (pl.n_splits + 1) * 32 * (int64_t)(D + 2) * (int64_t)sizeof(float);
+  return pl;
+}
+}  // namespace
+
+int dspark_draft_attention_workspace_bytes(int64_t num_requests, int32_t block,
+                                           int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int64_t max_prefix, int64_t* bytes) {
+  if (!bytes || num_requests < 0 || block < 1 || num_q_heads < 1 || num_kv_heads < 1 ||
+      num_q_heads % num_kv_heads != 0 || head_dim < 1 || max_prefix < 0)
+    return DSPARK_E_INVALID;
+  *bytes = attn_plan(num_requests, block, num_q_heads, num_kv_heads, head_dim, max_prefix,
+                     current_device_cus())
+               .bytes;
+  return DSPARK_OK;
+}
+
+int dspark_draft_attention(const dspark_attn_desc* d, int64_t num_requests, int32_t block,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t act_dtype, double sm_scale, int64_t max_prefix,
+                           void* workspace, int64_t workspace_bytes,
+                           unsigned long long* range_errors, void* stream_ptr,
+                           int32_t* fallback_reason) {
+  set_reason(fallback_reason, DSPARK_FB_NONE);
+  if (!d || num_requests < 0 || block < 1 || num_q_heads < 1 || num_kv_heads < 1 ||
+      num_q_heads % num_kv_heads != 0 || max_prefix < 0 || !(sm_scale == sm_scale))
+    return DSPARK_E_INVALID;
+  if (act_dtype != DSPARK_BF16 && act_dtype != DSPARK_FP16)
+    return fallback(fallback_reason, DSPARK_FB_DTYPE);
+  if (head_dim != 64 && head_dim != 128) return fallback(fallback_reason, DSPARK_FB_SHAPE);
+  if (num_requests == 0) return DSPARK_OK;
+  auto al16 = [](const void* ptr) { return reinterpret_cast<uintptr_t>(ptr) % 16 == 0; };
+  if (!d->q || !d->k_ext || !d->v_ext || !d->k_pool || !d->v_pool || !d->kv_indptr ||
+      !d->kv_indices || !d->out || !workspace || d->num_slots < 1)
+    return DSPARK_E_INVALID;
+  const int64_t strides[] = {d->q_token_stride, d->q_head_stride, d->ext_token_stride,
+                             d->ext_head_stride, d->pool_slot_stride, d->pool_head_stride,
+                             d->out_token_stride, d->out_head_stride};
+  for (int64_t st : strides)
+    if (st < head_dim || st % 8 != 0) return DSPARK_E_INVALID;
+  if (!al16(d->q) || !al16(d->k_ext) || !al16(d->v_ext) || !al16(d->k_pool) ||
+      !al16(d->v_pool) || !al16(d->out) || !al16(workspace))
+    return DSPARK_E_INVALID;
+  const int cus = current_device_cus();
+  if (cus <= 0) return DSPARK_E_DEVICE;
+  const AttnPlan pl = attn_plan(num_requests, block, num_q_heads, num_kv_heads, head_dim,
+                                max_prefix, cus);
+  if (workspace_bytes < pl.bytes) return DSPARK_E_INVALID;
+  dspark::AttnArgs a = {};
+  a.q = static_cast<const uint16_t*>(d->q);
+  a.k_ext = static_cast<const uint16_t*>(d->k_ext);
+  a.v_ext = static_cast<const uint16_t*>(d->v_ext);
+  a.k_pool = static_cast<const uint16_t*>(d->k_pool);
+  a.v_pool = static_cast<const uint16_t*>(d->v_pool);
+  a.kv_indptr = d->kv_indptr;
+  a.kv_indices = d->kv_indices;
+  a.out = static_cast<uint16_t*>(d->out);
+  a.part = static_cast<float*>(workspace);
+  a.err = range_errors;
+  a.q_stride0 = d->q_token_stride;
+  a.q_stride1 = d->q_head_stride;
+  a.ext_stride0 = d->ext_token_stride;
+  a.ext_stride1 = d->ext_head_stride;
+  a.pool_stride0 = d->pool_slot_stride;
+  a.pool_stride1 = d->pool_head_stride;
+  a.out_stride0 = d->out_token_stride;
+  a.out_stride1 = d->out_head_stride;
+  a.num_slots = d->num_slots;
+  a.B = num_requests;
+  a.split_len = pl.split_len;
+  a.max_prefix = max_prefix;
+  a.block = block;
+  a.nhk = num_kv_heads;
+  a.G = num_q_heads / num_kv_heads;
+  a.M = block * a.G;
+  a.row_tiles = pl.row_tiles;
+  a.n_splits = pl.n_splits;
+  a.sm_scale = (float)sm_scale;
+  const hipError_t e = dspark::launch_draft_attention(a, head_dim, act_dtype == DSPARK_FP16,
+                                                      static_cast<hipStream_t>(stream_ptr));
+  return e == hipSuccess ? DSPARK_OK : DSPARK_E_DEVICE;
+}

@@ -1,0 +1,314 @@
+// DSpark draft attention over the KV pool for gfx950: bidirectional
+// grouped-query attention of each request's block of queries over its prefix
+// (gathered from a layer's pool through the request's slot list) and the
+// block's own keys.
+//
+// Method: sglang PR #35499 ("K3 DSpark draft attention via verify_shared_kv on
+// ROCm gfx95", implementation breakdown and key source snippets): a split-KV
+// stage over the prefix, query head h reading KV head h // G, and a combine
+// stage with the causal mask off for the draft. Here the block's own keys are
+// one more split of the first stage, and the second stage only merges.
+//
+// Stage 1: one wave per (request, KV head, tile of 32 rows, key split). A row
+// is a (block token j, query head g of the group) pair, row = j * G + g. For
+// every 32 keys of the split:
+//   - S^T = K * Q^T on v_mfma_f32_32x32x16: keys on M (each lane gathers its
+//     key's row from the pool, 16 bytes per step), rows on N (Q fragments stay
+//     in registers). Lane l then holds row l % 32 and 16 of the 32 keys, so
+//     the online softmax (base-2, scores scaled by sm_scale * log2 e) is
+//     lane-local apart from one swap with lane l ^ 32.
+//   - O^T += V^T * P^T: the probabilities are the B operand straight from the
+//     score registers (the k-slots of a lane are exactly the keys it holds),
+//     and V^T comes from a transposed 32-key tile in LDS, read in the same key
+//     order. O^T's lane column is again the lane's row, so rescaling is
+//     lane-local.
+//   The split leaves fp32 (O, m, l) per row in the workspace.
+// Stage 2: per row, M = max m, L = sum l * 2^(m - M), O = sum O * 2^(m - M) / L,
+// rounded once to the dtype. Keys past a request's prefix, and slots outside
+// the pool (counted), are masked with a zero value row.
+#include "internal.h"
+
+namespace dspark {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+// LDS row of the V^T tile (elements): 72 bytes keeps 8-byte reads aligned, and
+// 32 consecutive rows start in 32 distinct even banks (18 d mod 64).
+constexpr int KS = 32 + 4;
+
+template <bool FP16>
+struct AE;
+
+template <>
+struct AE<false> {
+  using vec8 = bf16x8;
+  static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint16_t from_f(float f) {
+    return __builtin_bit_cast(uint16_t, (__bf16)f);  // round to nearest even
+  }
+};
+
+template <>
+struct AE<true> {
+  using vec8 = f16x8;
+  static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint16_t from_f(float f) {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);  // round to nearest even
+  }
+};
+
+__device__ __forceinline__ uint4 ld16(const uint16_t* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
+  const u32x4 v = *(global_u32x4*)p;
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+template <bool FP16, int D>
+__global__ __launch_bounds__(64) void draft_attn_stage1(const AttnArgs a) {
+  using E = AE<FP16>;
+  using vec8 = typename E::vec8;
+  constexpr int DS = D / 16;          // MFMA steps over the head dimension
+  constexpr int DB = D / 32;          // 32-wide blocks of O^T
+  constexpr int PPK = D / 8;          // 16-byte pieces per key row
+  constexpr int KPL = 64 / PPK;       // keys per V load instruction
+  constexpr int VLOADS = 32 / KPL;    // V load instructions per 32 keys
+  __shared__ __align__(16) uint16_t vt[D * KS];
+
+  const int lane = threadIdx.x;
+  const int r32 = lane & 31;
+  const int hh = lane >> 5;
+  int64_t wg = blockIdx.x;
+  const int nsp = a.n_splits + 1;
+  const int split = (int)(wg % nsp);
+  wg /= nsp;
+  const int rtile = (int)(wg % a.row_tiles);
+  wg /= a.row_tiles;
+  const int kh = (int)(wg % a.nhk);
+  const int64_t b = wg / a.nhk;
+
+  // this lane's row (N index of S^T and O^T)
+  const int row = rtile * 32 + r32;
+  const bool row_ok = row < a.M;
+  const int tj = row_ok ? row / a.G : 0;
+  const int tg = row_ok ? row % a.G : 0;
+  const int64_t qtok = b * a.block + tj;
+  vec8 qf[DS];
+  {
+    const uint16_t* qrow = a.q + qtok * a.q_stride0 + (int64_t)(kh * a.G + tg) * a.q_stride1;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      const uint4 u = row_ok ? ld16(qrow + 16 * s + 8 * hh) : make_uint4(0, 0, 0, 0);
+      qf[s] = __builtin_bit_cast(vec8, u);
+    }
+  }
+
+  const bool ext = split == a.n_splits;  // the block's own keys
+  const int64_t p0 = a.kv_indptr[b];
+  const int64_t plen = a.kv_indptr[b + 1] - p0;
+  const int64_t kbeg = ext ? 0 : (int64_t)split * a.split_len;
+  int64_t kend = ext ? a.block : kbeg + a.split_len;
+  // prefix keys past max_prefix are never attended (and counted below)
+  if (!ext) kend = min(kend, min(plen, a.max_prefix));
+  const uint16_t* kbase = ext ? a.k_ext : a.k_pool;
+  const uint16_t* vbase = ext ? a.v_ext : a.v_pool;
+  const bool counter = !ext && kh == 0 && rtile == 0 && a.err != nullptr;
+  // a prefix longer than max_prefix is counted once per request
+  if (ext && kh == 0 && rtile == 0 && a.err != nullptr && lane == 0 && plen > a.max_prefix)
+    atomicAdd(a.err, 1ull);
+  const float scale2 = a.sm_scale * kLog2e;
+
+  float m = -INFINITY, lsum = 0.0f;
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+
+  for (int64_t k0 = kbeg; k0 < kend; k0 += 32) {
+    // this lane's key (M index of S^T): its row in the pool or the block
+    const int64_t key = k0 + r32;
+    bool kvalid = key < kend;
+    int64_t krow = 0;  // element offset of the key's K/V row for this KV head
+    if (ext) {
+      krow = (b * a.block + (kvalid ? key : 0)) * a.ext_stride0 + (int64_t)kh * a.ext_stride1;
+    } else {
+      int64_t slot = kvalid ? a.kv_indices[p0 + key] : 0;
+      if (slot < 0 || slot >= a.num_slots) {
+        if (kvalid && counter && hh == 0) atomicAdd(a.err, 1ull);
+        kvalid = false;
+        slot = 0;
+      }
+      krow = slot * a.pool_stride0 + (int64_t)kh * a.pool_stride1;
+    }
+    const unsigned long long vmask = __ballot(kvalid);
+
+    // S^T = K * Q^T over the head dimension
+    f32x16 st;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st[r] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      const vec8 kf = __builtin_bit_cast(vec8, ld16(kbase + krow + 16 * s + 8 * hh));
+      st = E::mfma(kf, qf[s], st);
+    }
+
+    // V^T tile into LDS: vt[d][key], zero rows for masked keys
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i) {
+      const int kk = i * KPL + lane / PPK;  // key within the 32
+      const int piece = lane % PPK;
+      const int lo = __shfl((int)(krow & 0xFFFFFFFF), kk);
+      const int hi = __shfl((int)(krow >> 32), kk);
+      const int64_t vrow = ((int64_t)hi << 32) | (uint32_t)lo;
+      uint4 u = ld16(vbase + vrow + piece * 8);
+      if (!((vmask >> kk) & 1ull)) u = make_uint4(0, 0, 0, 0);
+      const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vt[(piece * 8 + 2 * e) * KS + kk] = (uint16_t)(w4[e] & 0xFFFFu);
+        vt[(piece * 8 + 2 * e + 1) * KS + kk] = (uint16_t)(w4[e] >> 16);
+      }
+    }
+
+    // online softmax of this lane's row over the 32 keys (16 here, 16 in lane ^ 32)
+    float sv[16];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kr = 8 * (r / 4) + 4 * hh + (r % 4);
+      sv[r] = ((vmask >> kr) & 1ull) ? st[r] * scale2 : -INFINITY;
+      mx = fmaxf(mx, sv[r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(m, mx);
+    const float alpha = mnew == -INFINITY ? 1.0f : exp2f(m - mnew);
+    float ps = 0.0f;
+    uint32_t pk[8];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float pa = sv[r] == -INFINITY ? 0.0f : exp2f(sv[r] - mnew);
+      const float pb = sv[r + 1] == -INFINITY ? 0.0f : exp2f(sv[r + 1] - mnew);
+      ps += pa + pb;
+      pk[r / 2] = (uint32_t)E::from_f(pa) | ((uint32_t)E::from_f(pb) << 16);
+    }
+    ps += __shfl_xor(ps, 32);
+    lsum = lsum * alpha + ps;
+    m = mnew;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+
+    // O^T += V^T * P^T: k-step s takes this lane's score registers 8s .. 8s + 7,
+    // i.e. keys 16s + 4h + [0, 4) and 16s + 8 + 4h + [0, 4)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const vec8 pf = __builtin_bit_cast(
+          vec8, make_uint4(pk[4 * s], pk[4 * s + 1], pk[4 * s + 2], pk[4 * s + 3]));
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const uint16_t* vr = vt + (db * 32 + r32) * KS + 16 * s + 4 * hh;
+        const uint2 x0 = *reinterpret_cast<const uint2*>(vr);
+        const uint2 x1 = *reinterpret_cast<const uint2*>(vr + 8);
+        const vec8 af = __builtin_bit_cast(vec8, make_uint4(x0.x, x0.y, x1.x, x1.y));
+        o[db] = E::mfma(af, pf, o[db]);
+      }
+    }
+  }
+
+  // partial record: O [32 rows][D] fp32, then m [32], then l [32]
+  float* rec = a.part + (((b * a.nhk + kh) * a.row_tiles + rtile) * nsp + split) *
+                            (int64_t)(32 * (D + 2));
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<float4*>(rec + r32 * D + db * 32 + 8 * q + 4 * hh) =
+          make_float4(o[db][4 * q], o[db][4 * q + 1], o[db][4 * q + 2], o[db][4 * q + 3]);
+  if (hh == 0) {
+    rec[32 * D + r32] = m;
+    rec[32 * D + 32 + r32] = lsum;
+  }
+}
+
+template <bool FP16, int D>
+__global__ __launch_bounds__(64) void draft_attn_stage2(const AttnArgs a) {
+  using E = AE<FP16>;
+  const int lane = threadIdx.x;
+  const int r32 = lane & 31;
+  const int hh = lane >> 5;
+  int64_t wg = blockIdx.x;
+  const int rtile = (int)(wg % a.row_tiles);
+  wg /= a.row_tiles;
+  const int kh = (int)(wg % a.nhk);
+  const int64_t b = wg / a.nhk;
+  const int row = rtile * 32 + r32;
+  if (row >= a.M) return;
+  const int nsp = a.n_splits + 1;
+  const float* base =
+      a.part + ((b * a.nhk + kh) * a.row_tiles + rtile) * nsp * (int64_t)(32 * (D + 2));
+  constexpr int64_t REC = 32 * (D + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < nsp; ++s) M = fmaxf(M, base[s * REC + 32 * D + r32]);
+  float L = 0.0f;
+  for (int s = 0; s < nsp; ++s) {
+    const float ms = base[s * REC + 32 * D + r32];
+    if (ms != -INFINITY) L += base[s * REC + 32 * D + 32 + r32] * exp2f(ms - M);
+  }
+  const float invL = 1.0f / L;
+  const int tj = row / a.G, tg = row % a.G;
+  uint16_t* out = a.out + (b * a.block + tj) * a.out_stride0 + (int64_t)(kh * a.G + tg) * a.out_stride1;
+  // this lane: half hh of the row's D features, 8 at a time
+#pragma unroll
+  for (int d0 = hh * (D / 2); d0 < (hh + 1) * (D / 2); d0 += 8) {
+    float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < nsp; ++s) {
+      const float ms = base[s * REC + 32 * D + r32];
+      if (ms == -INFINITY) continue;
+      const float wgt = exp2f(ms - M);
+      const float4 x0 = *reinterpret_cast<const float4*>(base + s * REC + r32 * D + d0);
+      const float4 x1 = *reinterpret_cast<const float4*>(base + s * REC + r32 * D + d0 + 4);
+      acc[0] += x0.x * wgt, acc[1] += x0.y * wgt, acc[2] += x0.z * wgt, acc[3] += x0.w * wgt;
+      acc[4] += x1.x * wgt, acc[5] += x1.y * wgt, acc[6] += x1.z * wgt, acc[7] += x1.w * wgt;
+    }
+    uint32_t w4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w4[e] = (uint32_t)E::from_f(acc[2 * e] * invL) |
+              ((uint32_t)E::from_f(acc[2 * e + 1] * invL) << 16);
+    *reinterpret_cast<uint4*>(out + d0) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+  }
+}
+
+template <bool FP16, int D>
+hipError_t launch(const AttnArgs& a, hipStream_t stream) {
+  const int64_t g1 = (int64_t)a.B * a.nhk * a.row_tiles * (a.n_splits + 1);
+  const int64_t g2 = (int64_t)a.B * a.nhk * a.row_tiles;
+  if (g1 > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((draft_attn_stage1<FP16, D>), dim3((uint32_t)g1), dim3(64), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((draft_attn_stage2<FP16, D>), dim3((uint32_t)g2), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_draft_attention(const AttnArgs& a, int head_dim, bool is_fp16,
+                                  hipStream_t stream) {
+  if (a.B <= 0) return hipSuccess;
+  if (head_dim == 128) return is_fp16 ? launch<true, 128>(a, stream) : launch<false, 128>(a, stream);
+  if (head_dim == 64) return is_fp16 ? launch<true, 64>(a, stream) : launch<false, 64>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dspark

@@ -98,6 +98,36 @@ hipError_t launch_row_norm(uint16_t* y, int64_t y_stride, const float* partial, 
                            int64_t groups, int ksplits, const float* g, float eps, bool is_fp16,
                            hipStream_t stream);
 
+// Arguments of the draft attention (element strides).
+struct AttnArgs {
+  const uint16_t* q;        // [B * block, nhq, D]
+  const uint16_t* k_ext;    // [B * block, nhk, D] (the block's own keys)
+  const uint16_t* v_ext;
+  const uint16_t* k_pool;   // [num_slots, nhk, D]
+  const uint16_t* v_pool;
+  const int64_t* kv_indptr;   // [B + 1]
+  const int64_t* kv_indices;  // prefix slots
+  uint16_t* out;            // [B * block, nhq, D]
+  float* part;              // workspace: per split record O [32][D], m [32], l [32]
+  unsigned long long* err;  // skipped slots and uncovered prefixes, or nullptr
+  int64_t q_stride0, q_stride1;
+  int64_t ext_stride0, ext_stride1;
+  int64_t pool_stride0, pool_stride1;
+  int64_t out_stride0, out_stride1;
+  int64_t num_slots;
+  int64_t B;
+  int64_t split_len;        // prefix keys per split (multiple of 32)
+  int64_t max_prefix;       // prefix keys past this are not attended
+  int32_t block, nhk, G, M;  // M = block * G rows per (request, KV head)
+  int32_t row_tiles;        // ceil(M / 32)
+  int32_t n_splits;         // prefix splits; the block's keys are one more
+  float sm_scale;
+};
+
+// Launches the two draft-attention stages for `a` (validated by the caller).
+hipError_t launch_draft_attention(const AttnArgs& a, int head_dim, bool is_fp16,
+                                  hipStream_t stream);
+
 // Launches the fused GEMM + norm + rotation + scatter for `a` on `stream`.
 // `num_cus` (compute units of the device) sizes the small-T grid. Shapes have
 // been validated by the caller. Returns the launch status.

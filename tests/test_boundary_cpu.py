@@ -32,7 +32,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_struct_layouts_match_c(tmp_path):
     """The ctypes mirrors have the C compiler's size and field offsets."""
-    fields = {"dspark_layer_desc": dk.LayerDesc, "dspark_pool_desc": dk.PoolDesc}
+    fields = {"dspark_layer_desc": dk.LayerDesc, "dspark_pool_desc": dk.PoolDesc,
+              "dspark_attn_desc": dk.AttnDesc}
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "dspark.h"', "int main(void) {"]
     for cname, py in fields.items():
         lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
@@ -237,3 +238,41 @@ def test_proj_calls_reject_null_pack():
     assert lib.dspark_main_proj_workspace_bytes(None, 4, ctypes.byref(n)) == dk.E_INVALID
     assert lib.dspark_main_proj_norm(None, 16, 4, 768, 16, 256, 16, 1 << 20, None) == dk.E_INVALID
     lib.dspark_main_proj_free(None)  # no-op
+
+
+
+# ------------------------------------------------------------ draft attention
+
+def _attn(B=2, block=8, nhq=8, nhk=2, D=128, dtype=dk.BF16, max_prefix=100, ws=None, wsb=0,
+          **fields):
+    base = dict(q_token_stride=1024, q_head_stride=128, ext_token_stride=256,
+                ext_head_stride=128, pool_slot_stride=256, pool_head_stride=128, num_slots=64)
+    base.update(fields)
+    desc = dk.AttnDesc(**base)
+    r = ctypes.c_int32(-7)
+    st = dk.lib().dspark_draft_attention(ctypes.byref(desc), B, block, nhq, nhk, D, dtype, 0.1,
+                                         max_prefix, ws, wsb, None, None, ctypes.byref(r))
+    return st, r.value
+
+
+def test_attn_fallbacks_and_empty():
+    assert _attn(D=96) == (dk.FALLBACK, 6)
+    assert _attn(dtype=dk.FP32) == (dk.FALLBACK, 7)
+    assert _attn(B=0) == (dk.OK, 0)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(B=-1), dict(block=0), dict(nhq=6, nhk=4), dict(max_prefix=-1),
+    dict(),  # NULL tensors with work to do
+])
+def test_attn_invalid(kw):
+    assert _attn(**kw)[0] == dk.E_INVALID
+
+
+def test_attn_workspace_size_formula():
+    """One fp32 record of 32 x (D + 2) per request, KV head, 32-row tile and
+    split (the block's own keys are one more split than the prefix needs)."""
+    n = dk.draft_attention_workspace_bytes(2, 8, 8, 2, 128, 0)
+    assert n == 2 * 2 * 1 * 1 * 32 * 130 * 4  # no prefix: one split
+    m = dk.draft_attention_workspace_bytes(2, 8, 8, 2, 128, 100000)
+    assert m % (2 * 2 * 32 * 130 * 4) == 0 and m > n
