@@ -7,7 +7,8 @@ Prints ONE JSON line on stdout; progress goes to stderr. The workloads
 qk_decode and qk_prefill_8k time the in-place table QK-RMSNorm + neox RoPE
 (dspark_table_qk_norm_rope) instead, one call per step, and verify_decode and
 verify_wide time the accept length + bonus token (dspark_verify_accept), and
-proj_decode and proj_prefill_8k the context producer (dspark_main_proj_norm).
+proj_decode and proj_prefill_8k the context producer (dspark_main_proj_norm),
+and attn_decode_8k and attn_d64_16k the draft attention (dspark_draft_attention).
 
 Timing: W warmup steps, then exactly K steps, each bracketed by a device
 synchronisation. The steps are captured into a HIP graph first, so host launch
@@ -41,6 +42,8 @@ QK_KERNEL_SOURCE = os.path.join(CSRC, "qk_norm_rope.hip")
 QK_METRIC = "in-place QK-RMSNorm+RoPE tokens/s; % of HBM roofline"
 VERIFY_KERNEL_SOURCE = os.path.join(CSRC, "verify_accept.hip")
 PROJ_METRIC = "context-producer tokens/s (main_proj GEMM + main_norm); % of MFMA/HBM roofline"
+ATTN_KERNEL_SOURCE = os.path.join(CSRC, "draft_attention.hip")
+ATTN_METRIC = "draft-attention query tokens/s over the KV pool; % of HBM roofline"
 VERIFY_METRIC = "verify accept-length + bonus requests/s; % of HBM roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_PROBE_BYTES = 1 << 30
@@ -87,9 +90,14 @@ def is_proj(workload: str) -> bool:
     return workload.startswith("proj_")
 
 
+def is_attn(workload: str) -> bool:
+    return workload.startswith("attn_")
+
+
 def kernel_source_hash(workload: str = "") -> str:
     src = (QK_KERNEL_SOURCE if is_qk(workload) else
-           VERIFY_KERNEL_SOURCE if is_verify(workload) else KERNEL_SOURCE)
+           VERIFY_KERNEL_SOURCE if is_verify(workload) else
+           ATTN_KERNEL_SOURCE if is_attn(workload) else KERNEL_SOURCE)
     with open(src, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
@@ -250,7 +258,8 @@ def time_steps(step, steps: int, warmup: int, eager: bool):
 
 def roofline(alg: dict, t_kernel: float, workload: str) -> dict:
     ridge = MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if alg["flops"] / alg["bytes"] < ridge or is_qk(workload) or is_verify(workload):
+    if (alg["flops"] / alg["bytes"] < ridge or is_qk(workload) or is_verify(workload)
+            or is_attn(workload)):
         ach = alg["bytes"] / t_kernel / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4)}
@@ -449,6 +458,87 @@ def run_proj(args) -> int:
     return 0
 
 
+def run_attn(args) -> int:
+    """Draft attention on an attn workload; one dspark_draft_attention (two
+    launches) per step. Algorithmic bytes: each request's prefix K and V rows
+    read once per KV head, the block's queries, own K/V and outputs, the slot
+    list; pools smaller than twice the Infinity Cache rotate over copies."""
+    import numpy as np
+    import torch
+
+    import speculative_decoding_draft_stacked_amd as dk
+    from speculative_decoding_draft_stacked_amd import workloads as W
+
+    c = W.attn_workload(args.workload)
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16}[c.dtype]
+    dev16 = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(tdt).cuda()
+    q, ke, ve = dev16(c.q), dev16(c.k_ext), dev16(c.v_ext)
+    pool_bytes = 2 * c.k_pool.nbytes
+    copies = max(1, math.ceil(2 * INFINITY_CACHE_BYTES / pool_bytes))
+    pools = [(dev16(c.k_pool), dev16(c.v_pool)) for _ in range(copies)]
+    indptr = torch.from_numpy(c.kv_indptr).cuda()
+    indices = torch.from_numpy(c.kv_indices).cuda()
+    out = torch.empty_like(q)
+    ws = torch.empty(dk.draft_attention_workspace_bytes(c.B, c.block, c.nhq, c.nhk, c.D,
+                                                        c.max_prefix), dtype=torch.uint8,
+                     device="cuda")
+    err = torch.zeros(1, dtype=torch.int64, device="cuda")
+    keys = int(c.kv_indptr[-1])
+    T = c.B * c.block
+    nbytes = float(keys * c.nhk * c.D * 2 * 2 + T * (c.nhq + 2 * c.nhk + c.nhq) * c.D * 2
+                   + 8 * keys + 8 * (c.B + 1))
+    flops = 4.0 * T * c.nhq * c.D * (keys / c.B + c.block)
+    alg = {"flops": flops, "bytes": nbytes}
+    log(f"[bench] B={c.B} block={c.block} heads {c.nhq}/{c.nhk} D={c.D} prefix {c.max_prefix}, "
+        f"pool copies {copies}")
+
+    def step(i):
+        kp, vp = pools[i % copies]
+        if not dk.draft_attention(q, ke, ve, kp, vp, indptr, indices, out, c.block, c.sm_scale,
+                                  c.max_prefix, ws, err):
+            raise RuntimeError("attention fell back")
+
+    gpu_ms, wall, launch = time_steps(step, args.steps, args.warmup, args.eager)
+    assert int(err.item()) == 0
+    ms_per_step = gpu_ms / args.steps
+    t_kernel = ms_per_step * 1e-3
+    out_line = {
+        "metric": ATTN_METRIC, "value": round(T / t_kernel, 1), "unit": "query tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": c.dtype,
+        "data": "synthetic: seeded queries, pools and slot lists of the workload's shape",
+        "config": {"workload": args.workload, "requests": c.B, "block": c.block,
+                   "q_heads": c.nhq, "kv_heads": c.nhk, "head_dim": c.D,
+                   "prefix": c.max_prefix, "pool_copies": copies, "launch": launch,
+                   "launches_per_step": 2, "algorithmic_bytes": nbytes, "flops": flops},
+        "roofline": roofline(alg, t_kernel, args.workload),
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+        from oracle import draft_attention_oracle as A
+        reps, t0 = 0, time.perf_counter()
+        while True:  # one request per pass (the whole batch would take minutes)
+            b = reps % c.B
+            r = slice(b * c.block, (b + 1) * c.block)
+            idx = c.kv_indices[c.kv_indptr[b]:c.kv_indptr[b + 1]]
+            A.draft_attention(c.q[r], c.k_ext[r], c.v_ext[r], c.k_pool, c.v_pool,
+                              [0, len(idx)], idx, c.block, c.nhq, c.nhk, c.sm_scale, c.dtype)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        out_line["cpu_baseline"] = {
+            "value": c.block * reps / el, "unit": "query tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{reps} requests of the {c.name} batch ({c.block} queries, "
+                      f"{c.max_prefix}-key prefix each) in {el:.1f} s; numpy fp64, BLAS "
+                      f"threads = {threads}"}
+    print(json.dumps(out_line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -497,6 +587,8 @@ def main() -> int:
         return run_verify(args)
     if is_proj(args.workload):
         return run_proj(args)
+    if is_attn(args.workload):
+        return run_attn(args)
 
     log(f"[bench] generating workload {args.workload}")
     case = W.workload(args.workload)
