@@ -24,7 +24,7 @@
 //     lane-local.
 //   The split leaves fp32 (O, m, l) per row in the workspace.
 // Stage 2: per row, M = max m, L = sum l * 2^(m - M), O = sum O * 2^(m - M) / L,
-// rounded once to the dtype. Keys past a request's prefix, and slots outside
+// rounded once to the dtype; a thread per (row, 8 features). Keys past a request's prefix, and slots outside
 // the pool (counted), are masked with a zero value row.
 #include "internal.h"
 
@@ -133,43 +133,37 @@ __global__ __launch_bounds__(64) void draft_attn_stage1(const AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
 
-  for (int64_t k0 = kbeg; k0 < kend; k0 += 32) {
-    // this lane's key (M index of S^T): its row in the pool or the block
-    const int64_t key = k0 + r32;
-    bool kvalid = key < kend;
-    int64_t krow = 0;  // element offset of the key's K/V row for this KV head
-    if (ext) {
-      krow = (b * a.block + (kvalid ? key : 0)) * a.ext_stride0 + (int64_t)kh * a.ext_stride1;
-    } else {
-      int64_t slot = kvalid ? a.kv_indices[p0 + key] : 0;
-      if (slot < 0 || slot >= a.num_slots) {
-        if (kvalid && counter && hh == 0) atomicAdd(a.err, 1ull);
-        kvalid = false;
-        slot = 0;
-      }
-      krow = slot * a.pool_stride0 + (int64_t)kh * a.pool_stride1;
+  // Keys go in windows of 8 steps of 32: the window's slot indices are loaded
+  // at once, and each step's K and V gathers are issued one step ahead into
+  // alternating registers, so the gathers overlap the previous step's math.
+  constexpr int WSTEPS = 8;
+  uint4 kf[2][DS], vu[2][VLOADS];
+  auto load_kv = [&](int64_t krow, uint4(&kd)[DS], uint4(&vd)[VLOADS]) {
+#pragma unroll
+    for (int s = 0; s < DS; ++s) kd[s] = ld16(kbase + krow + 16 * s + 8 * hh);
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i) {
+      const int kk = i * KPL + lane / PPK;  // key within the 32
+      const int lo = __shfl((int)(krow & 0xFFFFFFFF), kk);
+      const int hi = __shfl((int)(krow >> 32), kk);
+      const int64_t vrow = ((int64_t)hi << 32) | (uint32_t)lo;
+      vd[i] = ld16(vbase + vrow + (lane % PPK) * 8);
     }
-    const unsigned long long vmask = __ballot(kvalid);
-
+  };
+  auto step = [&](const uint4(&kd)[DS], const uint4(&vd)[VLOADS], unsigned long long vmask) {
     // S^T = K * Q^T over the head dimension
     f32x16 st;
 #pragma unroll
     for (int r = 0; r < 16; ++r) st[r] = 0.0f;
 #pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      const vec8 kf = __builtin_bit_cast(vec8, ld16(kbase + krow + 16 * s + 8 * hh));
-      st = E::mfma(kf, qf[s], st);
-    }
+    for (int s = 0; s < DS; ++s) st = E::mfma(__builtin_bit_cast(vec8, kd[s]), qf[s], st);
 
     // V^T tile into LDS: vt[d][key], zero rows for masked keys
 #pragma unroll
     for (int i = 0; i < VLOADS; ++i) {
-      const int kk = i * KPL + lane / PPK;  // key within the 32
+      const int kk = i * KPL + lane / PPK;
       const int piece = lane % PPK;
-      const int lo = __shfl((int)(krow & 0xFFFFFFFF), kk);
-      const int hi = __shfl((int)(krow >> 32), kk);
-      const int64_t vrow = ((int64_t)hi << 32) | (uint32_t)lo;
-      uint4 u = ld16(vbase + vrow + piece * 8);
+      uint4 u = vd[i];
       if (!((vmask >> kk) & 1ull)) u = make_uint4(0, 0, 0, 0);
       const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -223,6 +217,37 @@ __global__ __launch_bounds__(64) void draft_attn_stage1(const AttnArgs a) {
         o[db] = E::mfma(af, pf, o[db]);
       }
     }
+  };
+
+  for (int64_t w0 = kbeg; w0 < kend; w0 += 32 * WSTEPS) {
+    // this lane's key of every step in the window (M index of S^T): its row
+    int64_t krow[WSTEPS];
+    unsigned long long vmask[WSTEPS];
+#pragma unroll
+    for (int j = 0; j < WSTEPS; ++j) {
+      const int64_t key = w0 + 32 * j + r32;
+      bool kvalid = key < kend;
+      if (ext) {
+        krow[j] = (b * a.block + (kvalid ? key : 0)) * a.ext_stride0 +
+                  (int64_t)kh * a.ext_stride1;
+      } else {
+        int64_t slot = kvalid ? a.kv_indices[p0 + key] : 0;
+        if (slot < 0 || slot >= a.num_slots) {
+          if (kvalid && counter && hh == 0) atomicAdd(a.err, 1ull);
+          kvalid = false;
+          slot = 0;
+        }
+        krow[j] = slot * a.pool_stride0 + (int64_t)kh * a.pool_stride1;
+      }
+      vmask[j] = __ballot(kvalid);
+    }
+    load_kv(krow[0], kf[0], vu[0]);
+#pragma unroll
+    for (int j = 0; j < WSTEPS; ++j) {
+      if (j + 1 < WSTEPS && w0 + 32 * (j + 1) < kend)  // uniform over the wave
+        load_kv(krow[j + 1], kf[(j + 1) & 1], vu[(j + 1) & 1]);
+      if (w0 + 32 * j < kend) step(kf[j & 1], vu[j & 1], vmask[j]);
+    }
   }
 
   // partial record: O [32 rows][D] fp32, then m [32], then l [32]
@@ -240,52 +265,56 @@ __global__ __launch_bounds__(64) void draft_attn_stage1(const AttnArgs a) {
   }
 }
 
+// Stage 2: one thread per (row, 8 features) of a (request, KV head, row tile)
+// record. Each thread recomputes its row's M and L from the per-split m and l
+// (cached loads) and adds the splits' O with weights 2^(m - M), in split
+// order; an empty split has m = -inf, l = 0 and O = 0, so its weight is just
+// zero and the loop needs no branch (its loads stay in flight together).
 template <bool FP16, int D>
-__global__ __launch_bounds__(64) void draft_attn_stage2(const AttnArgs a) {
+__global__ __launch_bounds__(256) void draft_attn_stage2(const AttnArgs a) {
   using E = AE<FP16>;
-  const int lane = threadIdx.x;
-  const int r32 = lane & 31;
-  const int hh = lane >> 5;
+  constexpr int FG = D / 8;        // 8-feature groups of a row
+  constexpr int RPP = 256 / FG;    // rows per pass of the workgroup
+  constexpr int64_t REC = 32 * (D + 2);
+  const int tid = threadIdx.x;
+  const int fg = tid % FG;
   int64_t wg = blockIdx.x;
   const int rtile = (int)(wg % a.row_tiles);
   wg /= a.row_tiles;
   const int kh = (int)(wg % a.nhk);
   const int64_t b = wg / a.nhk;
-  const int row = rtile * 32 + r32;
-  if (row >= a.M) return;
   const int nsp = a.n_splits + 1;
-  const float* base =
-      a.part + ((b * a.nhk + kh) * a.row_tiles + rtile) * nsp * (int64_t)(32 * (D + 2));
-  constexpr int64_t REC = 32 * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < nsp; ++s) M = fmaxf(M, base[s * REC + 32 * D + r32]);
-  float L = 0.0f;
-  for (int s = 0; s < nsp; ++s) {
-    const float ms = base[s * REC + 32 * D + r32];
-    if (ms != -INFINITY) L += base[s * REC + 32 * D + 32 + r32] * exp2f(ms - M);
-  }
-  const float invL = 1.0f / L;
-  const int tj = row / a.G, tg = row % a.G;
-  uint16_t* out = a.out + (b * a.block + tj) * a.out_stride0 + (int64_t)(kh * a.G + tg) * a.out_stride1;
-  // this lane: half hh of the row's D features, 8 at a time
-#pragma unroll
-  for (int d0 = hh * (D / 2); d0 < (hh + 1) * (D / 2); d0 += 8) {
+  const float* base = a.part + ((b * a.nhk + kh) * a.row_tiles + rtile) * nsp * REC;
+  for (int r0 = 0; r0 < 32; r0 += RPP) {
+    const int r32 = r0 + tid / FG;
+    const int row = rtile * 32 + r32;
+    if (row >= a.M) continue;  // no barrier below
+    float M = -INFINITY;
+#pragma unroll 8
+    for (int s = 0; s < nsp; ++s) M = fmaxf(M, base[s * REC + 32 * D + r32]);
+    float L = 0.0f;
     float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 8
     for (int s = 0; s < nsp; ++s) {
-      const float ms = base[s * REC + 32 * D + r32];
-      if (ms == -INFINITY) continue;
-      const float wgt = exp2f(ms - M);
-      const float4 x0 = *reinterpret_cast<const float4*>(base + s * REC + r32 * D + d0);
-      const float4 x1 = *reinterpret_cast<const float4*>(base + s * REC + r32 * D + d0 + 4);
+      const float* rec = base + s * REC;
+      const float ms = rec[32 * D + r32];
+      const float wgt = exp2f(ms - M);  // 0 for an empty split (m = -inf)
+      L += rec[32 * D + 32 + r32] * wgt;
+      const float4 x0 = *reinterpret_cast<const float4*>(rec + r32 * D + fg * 8);
+      const float4 x1 = *reinterpret_cast<const float4*>(rec + r32 * D + fg * 8 + 4);
       acc[0] += x0.x * wgt, acc[1] += x0.y * wgt, acc[2] += x0.z * wgt, acc[3] += x0.w * wgt;
       acc[4] += x1.x * wgt, acc[5] += x1.y * wgt, acc[6] += x1.z * wgt, acc[7] += x1.w * wgt;
     }
+    const float invL = 1.0f / L;
+    const int tj = row / a.G, tg = row % a.G;
+    uint16_t* out = a.out + (b * a.block + tj) * a.out_stride0 +
+                    (int64_t)(kh * a.G + tg) * a.out_stride1 + fg * 8;
     uint32_t w4[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       w4[e] = (uint32_t)E::from_f(acc[2 * e] * invL) |
               ((uint32_t)E::from_f(acc[2 * e + 1] * invL) << 16);
-    *reinterpret_cast<uint4*>(out + d0) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    *reinterpret_cast<uint4*>(out) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
   }
 }
 
@@ -297,7 +326,7 @@ hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((draft_attn_stage1<FP16, D>), dim3((uint32_t)g1), dim3(64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((draft_attn_stage2<FP16, D>), dim3((uint32_t)g2), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL((draft_attn_stage2<FP16, D>), dim3((uint32_t)g2), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
