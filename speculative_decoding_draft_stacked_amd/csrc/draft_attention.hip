@@ -13,8 +13,8 @@
 // is a (block token j, query head g of the group) pair, row = j * G + g. For
 // every 32 keys of the split:
 //   - S^T = K * Q^T on v_mfma_f32_32x32x16: keys on M (each lane gathers its
-//     key's row from the pool, 16 bytes per step), rows on N (Q fragments stay
-//     in registers). Lane l then holds row l % 32 and 16 of the 32 keys, so
+//     key's row from the pool, 16 bytes per step, and its V row the same way),
+//     rows on N (Q fragments stay in registers). Lane l then holds row l % 32 and 16 of the 32 keys, so
 //     the online softmax (base-2, scores scaled by sm_scale * log2 e) is
 //     lane-local apart from one swap with lane l ^ 32.
 //   - O^T += V^T * P^T: the probabilities are the B operand straight from the
@@ -78,9 +78,6 @@ __global__ __launch_bounds__(64) void draft_attn_stage1(const AttnArgs a) {
   using vec8 = typename E::vec8;
   constexpr int DS = D / 16;          // MFMA steps over the head dimension
   constexpr int DB = D / 32;          // 32-wide blocks of O^T
-  constexpr int PPK = D / 8;          // 16-byte pieces per key row
-  constexpr int KPL = 64 / PPK;       // keys per V load instruction
-  constexpr int VLOADS = 32 / KPL;    // V load instructions per 32 keys
   __shared__ __align__(16) uint16_t vt[D * KS];
 
   const int lane = threadIdx.x;
@@ -137,20 +134,18 @@ __global__ __launch_bounds__(64) void draft_attn_stage1(const AttnArgs a) {
   // at once, and each step's K and V gathers are issued one step ahead into
   // alternating registers, so the gathers overlap the previous step's math.
   constexpr int WSTEPS = 8;
-  uint4 kf[2][DS], vu[2][VLOADS];
-  auto load_kv = [&](int64_t krow, uint4(&kd)[DS], uint4(&vd)[VLOADS]) {
+  // K and V are gathered alike: lane (key r32, half h) takes features
+  // 16s + 8h + [0, 8) of its key's row, which is the MFMA A layout for K and,
+  // written to the transposed tile, puts 32 consecutive keys of one feature
+  // row in one instruction (no bank conflicts between the 16-lane groups).
+  uint4 kf[2][DS], vu[2][DS];
+  auto load_kv = [&](int64_t krow, uint4(&kd)[DS], uint4(&vd)[DS]) {
 #pragma unroll
     for (int s = 0; s < DS; ++s) kd[s] = ld16(kbase + krow + 16 * s + 8 * hh);
 #pragma unroll
-    for (int i = 0; i < VLOADS; ++i) {
-      const int kk = i * KPL + lane / PPK;  // key within the 32
-      const int lo = __shfl((int)(krow & 0xFFFFFFFF), kk);
-      const int hi = __shfl((int)(krow >> 32), kk);
-      const int64_t vrow = ((int64_t)hi << 32) | (uint32_t)lo;
-      vd[i] = ld16(vbase + vrow + (lane % PPK) * 8);
-    }
+    for (int s = 0; s < DS; ++s) vd[s] = ld16(vbase + krow + 16 * s + 8 * hh);
   };
-  auto step = [&](const uint4(&kd)[DS], const uint4(&vd)[VLOADS], unsigned long long vmask) {
+  auto step = [&](const uint4(&kd)[DS], const uint4(&vd)[DS], unsigned long long vmask) {
     // S^T = K * Q^T over the head dimension
     f32x16 st;
 #pragma unroll
@@ -159,17 +154,16 @@ __global__ __launch_bounds__(64) void draft_attn_stage1(const AttnArgs a) {
     for (int s = 0; s < DS; ++s) st = E::mfma(__builtin_bit_cast(vec8, kd[s]), qf[s], st);
 
     // V^T tile into LDS: vt[d][key], zero rows for masked keys
+    const bool vok = (vmask >> r32) & 1ull;
 #pragma unroll
-    for (int i = 0; i < VLOADS; ++i) {
-      const int kk = i * KPL + lane / PPK;
-      const int piece = lane % PPK;
-      uint4 u = vd[i];
-      if (!((vmask >> kk) & 1ull)) u = make_uint4(0, 0, 0, 0);
+    for (int s = 0; s < DS; ++s) {
+      const uint4 u = vok ? vd[s] : make_uint4(0, 0, 0, 0);
       const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+      uint16_t* col = vt + (16 * s + 8 * hh) * KS + r32;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        vt[(piece * 8 + 2 * e) * KS + kk] = (uint16_t)(w4[e] & 0xFFFFu);
-        vt[(piece * 8 + 2 * e + 1) * KS + kk] = (uint16_t)(w4[e] >> 16);
+        col[(2 * e) * KS] = (uint16_t)(w4[e] & 0xFFFFu);
+        col[(2 * e + 1) * KS] = (uint16_t)(w4[e] >> 16);
       }
     }
 
