@@ -741,11 +741,12 @@ int producer_ksplits(int64_t T, int64_t R, int64_t in_features, int64_t out_feat
                      int num_cus) {
   // Split K only where the write kernels' small-T path would run (so that the
   // grid is one round) and 128-token tiles alone leave the device
-  // under-filled; the row norm then holds a row in registers (<= 8192).
+  // under-filled; the row norm then holds a row in registers (<= 8192 features,
+  // a multiple of 512: four waves of whole 128-feature passes).
   if (num_cus < 1) num_cus = 1;
   const int64_t cap = R >= num_cus ? 1 : num_cus / R;
   const int64_t blocks32 = (T + 31) / 32;
-  if (blocks32 > 4 * cap || out_features > 8192) return 1;
+  if (blocks32 > 4 * cap || out_features > 8192 || out_features % 512 != 0) return 1;
   const int64_t tiles = R * ((T + 127) / 128);
   if (tiles >= num_cus) return 1;
   int64_t ks = num_cus / tiles;

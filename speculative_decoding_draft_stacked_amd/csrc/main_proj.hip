@@ -14,8 +14,9 @@
 // fp32 partial sums instead, and the norm kernel first adds a token's parts in
 // a fixed order and rounds them (the projection's output rounding).
 //
-// Mapping: one wave per token row, 16-byte accesses, 8 features per lane per
-// pass (a pass covers 512 features); sums across the wave use a butterfly,
+// Mapping: one wave per token row (a workgroup of four waves per token in the
+// K-split form, which has few tokens), 16-byte accesses, 8 features per lane
+// per pass (a pass covers 512 features); sums across the wave use a butterfly,
 // which leaves the same bits in every lane.
 #include "internal.h"
 
@@ -69,25 +70,29 @@ __global__ __launch_bounds__(kThreads) void row_norm_kernel(uint16_t* y, int64_t
 }
 
 // K-split form: partial holds ksplits fp32 partial projections [ks, T, H].
-// A wave adds its token's parts in order (deterministic), rounds to the dtype
-// (the linear's output rounding), keeps the row in registers (H <= 8192:
-// 16 passes of 512 features), and writes round(y * inv * g).
-constexpr int kMaxPasses = 16;
+// A workgroup of 4 waves takes one token: each wave adds the parts of a
+// quarter of the features in order (deterministic), rounds them to the dtype
+// (the linear's output rounding) and keeps them in registers (H <= 8192: up to
+// 4 passes of 512 features per wave); the four partial sums of squares are
+// added in wave order through LDS, and each wave writes round(y * inv * g).
+constexpr int kMaxPasses = 4;
 
 template <bool FP16>
 __global__ __launch_bounds__(kThreads) void row_norm_split_kernel(uint16_t* y, int64_t y_stride,
                                                                    const float* partial,
                                                                    int64_t T, int64_t H, int ks,
                                                                    const float* g, float eps) {
+  __shared__ float wsum[kThreads / 64];
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (t >= T) return;  // uniform over the wave
+  const int wave = threadIdx.x >> 6;
+  const int64_t t = blockIdx.x;
+  const int64_t quarter = H / 4;  // H % 512 == 0, so a quarter is whole passes of 128
   uint32_t yv[kMaxPasses][4];
   float ss = 0.0f;
 #pragma unroll
   for (int pp = 0; pp < kMaxPasses; ++pp) {
-    const int64_t c = (int64_t)pp * 512 + lane * 8;
-    if (c < H) {
+    const int64_t c = wave * quarter + (int64_t)pp * 512 + lane * 8;
+    if ((int64_t)pp * 512 + lane * 8 < quarter) {
       float sum[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
       for (int q = 0; q < ks; ++q) {
         const float* src = partial + ((int64_t)q * T + t) * H + c;
@@ -107,12 +112,15 @@ __global__ __launch_bounds__(kThreads) void row_norm_split_kernel(uint16_t* y, i
   }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
-  const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+  if (lane == 0) wsum[wave] = ss;
+  __syncthreads();
+  const float tot = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
   uint16_t* row = y + t * y_stride;
 #pragma unroll
   for (int pp = 0; pp < kMaxPasses; ++pp) {
-    const int64_t c = (int64_t)pp * 512 + lane * 8;
-    if (c < H) {
+    const int64_t c = wave * quarter + (int64_t)pp * 512 + lane * 8;
+    if ((int64_t)pp * 512 + lane * 8 < quarter) {
       const float4 g0 = *reinterpret_cast<const float4*>(g + c);
       const float4 g1 = *reinterpret_cast<const float4*>(g + c + 4);
       const float gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
@@ -138,14 +146,15 @@ hipError_t launch_row_norm(uint16_t* y, int64_t y_stride, const float* partial, 
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((uint32_t)blocks), block(kThreads);
   if (ksplits > 1) {
+    // a workgroup per token; a wave per quarter of the features
     const int64_t H = groups * 128;
-    if (H > kMaxPasses * 512) return hipErrorInvalidValue;
+    if (H > 4 * kMaxPasses * 512 || H % 512 != 0 || T > 0x7FFFFFFF) return hipErrorInvalidValue;
     if (is_fp16)
-      hipLaunchKernelGGL(row_norm_split_kernel<true>, grid, block, 0, stream, y, y_stride,
-                         partial, T, H, ksplits, g, eps);
+      hipLaunchKernelGGL(row_norm_split_kernel<true>, dim3((uint32_t)T), block, 0, stream, y,
+                         y_stride, partial, T, H, ksplits, g, eps);
     else
-      hipLaunchKernelGGL(row_norm_split_kernel<false>, grid, block, 0, stream, y, y_stride,
-                         partial, T, H, ksplits, g, eps);
+      hipLaunchKernelGGL(row_norm_split_kernel<false>, dim3((uint32_t)T), block, 0, stream, y,
+                         y_stride, partial, T, H, ksplits, g, eps);
   } else if (is_fp16) {
     hipLaunchKernelGGL(row_norm_kernel<true>, grid, block, 0, stream, y, y_stride, partial, T,
                        groups, g, eps);
