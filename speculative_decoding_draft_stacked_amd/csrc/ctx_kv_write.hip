@@ -107,9 +107,10 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
 // each V head, and scatter both into the token's slot of the head's layer pool.
 // Each (token, head) is handled by D/16 lanes; lane j owns elements
 // [8j, 8j+8) of the first half and their rotation partners 8j + D/2 + [0, 8).
+// With a row map (rmap != nullptr), tile token tt is row rmap[tt] (< 0: none).
 template <typename E, int D, int BT, bool COMMIT, int LDO, int NT = NTHREADS, int ROWS = BN>
 __device__ __forceinline__ void scatter_tile(const WriteArgs& a, const uint16_t* sO, int64_t n0,
-                                             int64_t t0, int tid) {
+                                             int64_t t0, int tid, const int* rmap = nullptr) {
   const int64_t T = a.T;
   constexpr int TPH = D / 16;    // lanes per (token, head)
   constexpr int HPT = ROWS / D;  // heads per tile
@@ -122,8 +123,8 @@ __device__ __forceinline__ void scatter_tile(const WriteArgs& a, const uint16_t*
     const int j = idx % TPH;
     const int tt = task / HPT;
     const int hd = task % HPT;
-    const int64_t t = t0 + tt;
-    if (t >= T) continue;  // uniform over the TPH lanes of a task
+    const int64_t t = rmap ? (int64_t)rmap[tt] : t0 + tt;
+    if (t < 0 || t >= T) continue;  // uniform over the TPH lanes of a task
     const int64_t loc = a.locs[t];
     bool valid = loc >= 0;
     if (COMMIT) valid = valid && (t % a.W) < a.commit[t / a.W];
@@ -442,6 +443,49 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
     scatter_tile<E, D, BT, COMMIT, LDO, NT, ROWS>(a, sO, n0, t0, tid);
 }
 
+// Row compaction for commit windows. Only rows that are written (slot >= 0
+// and inside the request's committed prefix) need projecting, so the rows of
+// a commit window are first numbered in row order over the valid ones, and
+// valid row j goes to token split j % splits, tile slot j / splits: the splits
+// share the valid rows evenly without the host knowing their count. Every
+// workgroup runs the same scan (T is small on this path). map[slot] = row, or
+// -1 where the slot holds none; returns this split's number of rows.
+template <int BT>
+__device__ int compact_rows(const WriteArgs& a, int64_t sp, int splits, int* map, int* wcnt,
+                            int tid) {
+  constexpr int NT = 512;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  for (int i = tid; i < BT; i += NT) map[i] = -1;
+  int base = 0;
+  for (int64_t c = 0; c < a.T; c += NT) {
+    const int64_t t = c + tid;
+    bool v = false;
+    if (t < a.T) {
+      const int64_t loc = a.locs[t];
+      const int64_t committed = a.commit[t / a.W];
+      v = (loc >= 0) & ((t % a.W) < committed);
+    }
+    const unsigned long long m = __ballot(v);
+    if (lane == 0) wcnt[wave] = __popcll(m);
+    __syncthreads();
+    int pre = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) {
+      const int n = wcnt[i];
+      pre += i < wave ? n : 0;
+      tot += n;
+    }
+    if (v) {
+      const int j = base + pre + __popcll(m & ((1ull << lane) - 1ull));
+      if (j % splits == sp && j / splits < BT) map[j / splits] = (int)t;
+    }
+    base += tot;
+    __syncthreads();
+  }
+  return base > sp ? (int)((base - sp + splits - 1) / splits) : 0;
+}
+
 // Weight-streaming kernel for small T (decode-sized batches). A workgroup
 // owns one 128-row tile of the stacked weight and BT = 32*NB tokens; the host
 // picks the number of token splits so that the whole grid is one round of
@@ -456,6 +500,9 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
 //   - Chunks are consumed in groups of two (one per parity) with one barrier
 //     per group; loads run LOOK groups ahead, so each wait covers only the
 //     group about to be used.
+//   - Commit windows: the workgroup's tokens are its share of the written rows
+//     (compact_rows); 32-token blocks past that share skip their MFMAs, and
+//     tile slots without a row load from the zero page.
 template <bool FP16, int D, bool BIAS, bool COMMIT, int NB>
 __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, int splits) {
   using E = Elem<FP16>;
@@ -463,6 +510,7 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
   constexpr int NT = 512;
   constexpr int BT = 32 * NB;
   constexpr int LOOK = 3;             // groups issued ahead of the one being computed
+  static_assert(LOOK == 3, "the commit-window prologue waits below assume three groups ahead");
   constexpr int SLOTS = LOOK + 1;     // per-wave weight ring slots (one chunk per group)
   constexpr int XSTAGES = 2 * SLOTS;  // X stages (one chunk each)
   constexpr int SXE = BT * BK;        // X stage elements
@@ -473,7 +521,10 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
   constexpr int XBYTES = XSTAGES * SXE * 2;
   constexpr int EBYTES = BT * RS * 4 + BT * LDO * 2;
   static_assert(XPW * 256 * 8 == SXE, "X chunk split");
-  __shared__ __align__(16) uint16_t smem[(XBYTES > EBYTES ? XBYTES : EBYTES) / 2];
+  constexpr int MBYTES = COMMIT ? (BT + NT / 64) * 4 : 0;  // row map + scan counts
+  __shared__ __align__(16) uint16_t smem[((XBYTES > EBYTES ? XBYTES : EBYTES) + MBYTES) / 2];
+  int* const rmap = reinterpret_cast<int*>(smem + (XBYTES > EBYTES ? XBYTES : EBYTES) / 2);
+  int* const wcnt = rmap + BT;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -510,7 +561,6 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
   const int nk = (int)((kq + 1) * nk_all / ks) - kc0;
   const int ng = (nk + 1) / 2;
   const int ng_ring = (ng + SLOTS - 1) / SLOTS * SLOTS;
-
   // this wave's pieces of weight block (rt, c): one contiguous KiB per MFMA step
   const uint16_t* wblk = a.w + (rt * nk_all + kc0) * 8192 + (w * 4 * 64 + lane) * 8;
   // X direct loads: instruction i of wave (w, par) fills LDS slots
@@ -519,32 +569,57 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
   // the same for every chunk.
   int64_t xoff[XPW];
   int xcol[XPW];
-#pragma unroll
-  for (int i = 0; i < XPW; ++i) {
-    const int slot = i * 256 + w * 64 + lane;
-    const int t = slot / 8;
-    const int piece = (slot % 8) ^ ((t >> 1) & 7);
-    const int64_t tok = t0 + t < T ? t0 + t : T - 1;  // rows past T are never stored
-    xoff[i] = tok * a.x_stride + piece * 8;
-    xcol[i] = piece * 8;
-  }
+  bool xrow[XPW];  // the slot holds a row (else it loads zeros)
 
   uint4 wq[SLOTS][4];
-  auto issue = [&](int g, uint4(&wd)[4]) {
+  auto issue_w = [&](int g, uint4(&wd)[4]) {
     const int c = 2 * g + par;  // chunk of this part (the stage follows it)
     const bool live = c < nk;   // chunks past the end read the zero page
     const uint16_t* wsrc = live ? wblk + (int64_t)c * 8192 : a.zeros;
     const int wstep = live ? 512 : 0;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) wd[kk] = ldg16(wsrc + kk * wstep);
+  };
+  auto issue_x = [&](int g) {
+    const int c = 2 * g + par;
+    const bool live = c < nk;
     uint16_t* stage = smem + ((c % XSTAGES) * SXE);
     const int kbase = (kc0 + c) * BK;
 #pragma unroll
     for (int i = 0; i < XPW; ++i) {
-      const bool ok = live && kbase + xcol[i] < H;
+      const bool ok = live && xrow[i] && kbase + xcol[i] < H;
       ldg16_to_lds(ok ? a.x + xoff[i] + kbase : a.zeros, stage + (i * 256 + w * 64) * 8);
     }
   };
+
+  // Commit windows: the weight loads of the first LOOK groups go out before
+  // the row scan, whose latency they then cover; the X loads follow it.
+  if constexpr (COMMIT) {
+#pragma unroll
+    for (int g = 0; g < LOOK; ++g) issue_w(g, wq[g]);
+    const int mine = compact_rows<BT>(a, sp, splits, rmap, wcnt, tid);
+    if (mine == 0) {  // uniform: nothing of this split is written
+      wait_vmcnt<0>();
+      return;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < XPW; ++i) {
+    const int slot = i * 256 + w * 64 + lane;
+    const int t = slot / 8;
+    const int piece = (slot % 8) ^ ((t >> 1) & 7);
+    int64_t tok;
+    if constexpr (COMMIT) {
+      tok = rmap[t];
+      xrow[i] = tok >= 0;
+      tok = xrow[i] ? tok : 0;
+    } else {
+      tok = t0 + t < T ? t0 + t : T - 1;  // rows past T are never stored
+      xrow[i] = true;
+    }
+    xoff[i] = tok * a.x_stride + piece * 8;
+    xcol[i] = piece * 8;
+  }
 
   f32x16 acc[NB];
 #pragma unroll
@@ -553,13 +628,25 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
     for (int r = 0; r < 16; ++r) acc[tb][r] = 0.0f;
 
 #pragma unroll
-  for (int g = 0; g < LOOK; ++g) issue(g, wq[g]);
+  for (int g = 0; g < LOOK; ++g) {
+    if constexpr (!COMMIT) issue_w(g, wq[g]);
+    issue_x(g);
+  }
   for (int g0 = 0; g0 < ng_ring; g0 += SLOTS) {
 #pragma unroll
     for (int u = 0; u < SLOTS; ++u) {
-      wait_ring<(LOOK - 1) * LOADS>();  // this thread's loads of group g0 + u landed
-      raw_barrier();                     // ... and everyone's; group g0 + u - 1 is free
-      issue(g0 + u + LOOK, wq[(u + LOOK) % SLOTS]);
+      // this thread's loads of group g0 + u have landed (in issue order: the
+      // first two waits of a commit-window prologue, which issued its weight
+      // loads ahead of all X loads, leave fewer loads outstanding)
+      if (COMMIT && u == 0 && g0 == 0)
+        wait_ring<(LOOK - 1) * XPW>();
+      else if (COMMIT && u == 1 && g0 == 0)
+        wait_ring<(LOOK - 2) * XPW + LOADS>();
+      else
+        wait_ring<(LOOK - 1) * LOADS>();
+      raw_barrier();  // ... and everyone's; group g0 + u - 1 is free
+      issue_w(g0 + u + LOOK, wq[(u + LOOK) % SLOTS]);
+      issue_x(g0 + u + LOOK);
       const uint16_t* xs = smem + ((2 * u + par) % XSTAGES) * SXE;
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
@@ -636,7 +723,7 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
   if constexpr (D == kRowsOut)
     rows_out_tile<E, BT, LDO, NT, BN>(a, sO, n0, t0, tid);
   else
-    scatter_tile<E, D, BT, COMMIT, LDO, NT>(a, sO, n0, t0, tid);
+    scatter_tile<E, D, BT, COMMIT, LDO, NT>(a, sO, n0, t0, tid, COMMIT ? rmap : nullptr);
 }
 
 template <bool FP16, int D, bool BIAS, bool COMMIT, int BT>
