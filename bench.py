@@ -54,16 +54,18 @@ def log(*a):
 
 
 def algorithmic(case, written_rows: int) -> dict:
-    """Algorithmic FLOPs and HBM bytes of one write: every row is projected;
-    bytes = stacked weight + hidden + bias + fp32 k_norm + one table row per
-    token + index arrays + the written pool rows."""
+    """Algorithmic FLOPs and HBM bytes of one write: what the stored rows
+    need. Only rows that are written need projecting, so flops = 2 x written
+    rows x stacked rows x H; bytes = stacked weight (+ bias) + fp32 k_norm
+    + per written row its hidden row, table row, position and pool rows
+    + every row's slot index + the commit lengths."""
     s = 2
     n_tot = case.n_tot
-    flops = 2.0 * case.T * n_tot * case.H
-    nbytes = (n_tot * case.H * s + case.T * case.H * s
-              + (n_tot * s if case.qkv_b is not None else 0)
-              + case.L * case.D * 4 + case.T * case.D * 4 + 16 * case.T
-              + 8 * case.num_requests + written_rows * n_tot * s)
+    flops = 2.0 * written_rows * n_tot * case.H
+    nbytes = (n_tot * case.H * s + (n_tot * s if case.qkv_b is not None else 0)
+              + case.L * case.D * 4
+              + written_rows * (case.H * s + case.D * 4 + 8 + n_tot * s)
+              + 8 * case.T + 8 * case.num_requests)
     return {"flops": flops, "bytes": float(nbytes)}
 
 

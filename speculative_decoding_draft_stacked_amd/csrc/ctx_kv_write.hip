@@ -32,6 +32,8 @@
 // 16-byte vectors into the pool row of the token's slot.
 #include "internal.h"
 
+#include <type_traits>
+
 namespace dspark {
 namespace {
 
@@ -594,10 +596,12 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
 
   // Commit windows: the weight loads of the first LOOK groups go out before
   // the row scan, whose latency they then cover; the X loads follow it.
+  int nbe = NB;  // 32-token blocks that hold rows
   if constexpr (COMMIT) {
 #pragma unroll
     for (int g = 0; g < LOOK; ++g) issue_w(g, wq[g]);
     const int mine = compact_rows<BT>(a, sp, splits, rmap, wcnt, tid);
+    nbe = (mine + 31) / 32;
     if (mine == 0) {  // uniform: nothing of this split is written
       wait_vmcnt<0>();
       return;
@@ -632,34 +636,47 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
     if constexpr (!COMMIT) issue_w(g, wq[g]);
     issue_x(g);
   }
-  for (int g0 = 0; g0 < ng_ring; g0 += SLOTS) {
+  // Main loop, instantiated for the number of 32-token blocks that hold rows
+  // (commit windows may fill fewer than NB): empty blocks issue no MFMAs.
+  auto main_loop = [&](auto nbe_c) {
+    constexpr int NBE = decltype(nbe_c)::value;
+    for (int g0 = 0; g0 < ng_ring; g0 += SLOTS) {
 #pragma unroll
-    for (int u = 0; u < SLOTS; ++u) {
-      // this thread's loads of group g0 + u have landed (in issue order: the
-      // first two waits of a commit-window prologue, which issued its weight
-      // loads ahead of all X loads, leave fewer loads outstanding)
-      if (COMMIT && u == 0 && g0 == 0)
-        wait_ring<(LOOK - 1) * XPW>();
-      else if (COMMIT && u == 1 && g0 == 0)
-        wait_ring<(LOOK - 2) * XPW + LOADS>();
-      else
-        wait_ring<(LOOK - 1) * LOADS>();
-      raw_barrier();  // ... and everyone's; group g0 + u - 1 is free
-      issue_w(g0 + u + LOOK, wq[(u + LOOK) % SLOTS]);
-      issue_x(g0 + u + LOOK);
-      const uint16_t* xs = smem + ((2 * u + par) % XSTAGES) * SXE;
+      for (int u = 0; u < SLOTS; ++u) {
+        // this thread's loads of group g0 + u have landed (in issue order: the
+        // first two waits of a commit-window prologue, which issued its weight
+        // loads ahead of all X loads, leave fewer loads outstanding)
+        if (COMMIT && u == 0 && g0 == 0)
+          wait_ring<(LOOK - 1) * XPW>();
+        else if (COMMIT && u == 1 && g0 == 0)
+          wait_ring<(LOOK - 2) * XPW + LOADS>();
+        else
+          wait_ring<(LOOK - 1) * LOADS>();
+        raw_barrier();  // ... and everyone's; group g0 + u - 1 is free
+        issue_w(g0 + u + LOOK, wq[(u + LOOK) % SLOTS]);
+        issue_x(g0 + u + LOOK);
+        const uint16_t* xs = smem + ((2 * u + par) % XSTAGES) * SXE;
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        const vec8 av = __builtin_bit_cast(vec8, wq[u][kk]);
+        for (int kk = 0; kk < BK / 16; ++kk) {
+          const vec8 av = __builtin_bit_cast(vec8, wq[u][kk]);
 #pragma unroll
-        for (int tb = 0; tb < NB; ++tb) {
-          const int t = tb * 32 + r32;
-          const int slot = (4 * hh + kk) ^ ((t >> 1) & 7);
-          const vec8 bv = *reinterpret_cast<const vec8*>(xs + (t * 8 + slot) * 8);
-          acc[tb] = E::mfma(av, bv, acc[tb]);
+          for (int tb = 0; tb < NBE; ++tb) {
+            const int t = tb * 32 + r32;
+            const int slot = (4 * hh + kk) ^ ((t >> 1) & 7);
+            const vec8 bv = *reinterpret_cast<const vec8*>(xs + (t * 8 + slot) * 8);
+            acc[tb] = E::mfma(av, bv, acc[tb]);
+          }
         }
       }
     }
+  };
+  if constexpr (COMMIT) {
+    if (NB >= 4 && nbe >= 4) main_loop(std::integral_constant<int, NB>{});
+    else if (NB >= 3 && nbe == 3) main_loop(std::integral_constant<int, NB >= 3 ? 3 : NB>{});
+    else if (NB >= 2 && nbe == 2) main_loop(std::integral_constant<int, NB >= 2 ? 2 : NB>{});
+    else main_loop(std::integral_constant<int, 1>{});
+  } else {
+    main_loop(std::integral_constant<int, NB>{});
   }
   wait_ring<0>();  // prefetches past the end (zero page) are done, LDS reads too
   raw_barrier();
