@@ -9,7 +9,8 @@
 // stage with the causal mask off for the draft. Here the block's own keys are
 // one more split of the first stage, and the second stage only merges.
 //
-// Stage 1: one wave per (request, KV head, tile of 32 rows, key split). A row
+// Stage 1: one wave per (request, KV head, tile of 32 rows, key split), the
+// heads of a record launched together on one XCD (see the record order). A row
 // is a (block token j, query head g of the group) pair, row = j * G + g. For
 // every 32 keys of the split:
 //   - S^T = K * Q^T on v_mfma_f32_32x32x16: keys on M (each lane gathers its
@@ -83,14 +84,26 @@ __global__ __launch_bounds__(64) void draft_attn_stage1(const AttnArgs a) {
   const int lane = threadIdx.x;
   const int r32 = lane & 31;
   const int hh = lane >> 5;
+  // Record order: the KV heads of one (request, row tile, split) are launched
+  // back to back on one XCD (workgroup w runs on XCD w % 8), so the pieces of
+  // each gathered pool row, one per head, reach HBM together and mostly hit an
+  // open DRAM row, rather than 256-byte reads scattered in time.
   int64_t wg = blockIdx.x;
   const int nsp = a.n_splits + 1;
+  const int64_t nrec = a.B * a.row_tiles * nsp;  // records per KV head
+  int kh;
+  if (nrec % 8 == 0) {
+    const int64_t q = wg / 8;
+    kh = (int)(q % a.nhk);
+    wg = (q / a.nhk) * 8 + wg % 8;
+  } else {
+    kh = (int)(wg % a.nhk);
+    wg /= a.nhk;
+  }
   const int split = (int)(wg % nsp);
   wg /= nsp;
   const int rtile = (int)(wg % a.row_tiles);
-  wg /= a.row_tiles;
-  const int kh = (int)(wg % a.nhk);
-  const int64_t b = wg / a.nhk;
+  const int64_t b = wg / a.row_tiles;
 
   // this lane's row (N index of S^T and O^T)
   const int row = rtile * 32 + r32;
