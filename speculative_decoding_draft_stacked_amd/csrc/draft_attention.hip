@@ -25,8 +25,9 @@
 //     lane-local.
 //   The split leaves fp32 (O, m, l) per row in the workspace.
 // Stage 2: per row, M = max m, L = sum l * 2^(m - M), O = sum O * 2^(m - M) / L,
-// rounded once to the dtype; a thread per (row, 8 features). Keys past a request's prefix, and slots outside
-// the pool (counted), are masked with a zero value row.
+// rounded once to the dtype; four threads per (row, 8 features), each merging a
+// quarter of the splits. Keys past a request's prefix, and slots outside the
+// pool (counted), are masked with a zero value row.
 #include "internal.h"
 
 namespace dspark {
@@ -272,64 +273,86 @@ __global__ __launch_bounds__(64) void draft_attn_stage1(const AttnArgs a) {
   }
 }
 
-// Stage 2: one thread per (row, 8 features) of a (request, KV head, row tile)
-// record. Each thread recomputes its row's M and L from the per-split m and l
-// (cached loads) and adds the splits' O with weights 2^(m - M), in split
-// order; an empty split has m = -inf, l = 0 and O = 0, so its weight is just
-// zero and the loop needs no branch (its loads stay in flight together).
+// Stage 2: four threads per (row, 8 features) of a (request, KV head, row
+// tile) record, each merging every fourth split online (running max M, sum L
+// and weighted O, rescaled as each split arrives, so its loads of all its
+// splits are independent and go out together); the four partial merges are
+// then combined by two lane swaps in a fixed order. An empty split has m =
+// -inf, l = 0 and O = 0 and adds nothing. A workgroup takes 256 / (4 * D / 8)
+// rows of a record, so short records still spread over many workgroups.
+constexpr int kMergeParts = 4;
+
 template <bool FP16, int D>
 __global__ __launch_bounds__(256) void draft_attn_stage2(const AttnArgs a) {
   using E = AE<FP16>;
-  constexpr int FG = D / 8;        // 8-feature groups of a row
-  constexpr int RPP = 256 / FG;    // rows per pass of the workgroup
+  constexpr int FG = D / 8;                     // 8-feature groups of a row
+  constexpr int P = kMergeParts;
+  constexpr int RPW = 256 / (P * FG);           // rows per workgroup
   constexpr int64_t REC = 32 * (D + 2);
+  static_assert(32 % RPW == 0, "row groups tile the 32-row record");
   const int tid = threadIdx.x;
-  const int fg = tid % FG;
+  const int part = tid % P;
+  const int fg = (tid / P) % FG;
   int64_t wg = blockIdx.x;
+  const int rgrp = (int)(wg % (32 / RPW));
+  wg /= 32 / RPW;
   const int rtile = (int)(wg % a.row_tiles);
   wg /= a.row_tiles;
   const int kh = (int)(wg % a.nhk);
   const int64_t b = wg / a.nhk;
   const int nsp = a.n_splits + 1;
   const float* base = a.part + ((b * a.nhk + kh) * a.row_tiles + rtile) * nsp * REC;
-  for (int r0 = 0; r0 < 32; r0 += RPP) {
-    const int r32 = r0 + tid / FG;
-    const int row = rtile * 32 + r32;
-    if (row >= a.M) continue;  // no barrier below
-    float M = -INFINITY;
-#pragma unroll 8
-    for (int s = 0; s < nsp; ++s) M = fmaxf(M, base[s * REC + 32 * D + r32]);
-    float L = 0.0f;
-    float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 8
-    for (int s = 0; s < nsp; ++s) {
-      const float* rec = base + s * REC;
-      const float ms = rec[32 * D + r32];
-      const float wgt = exp2f(ms - M);  // 0 for an empty split (m = -inf)
-      L += rec[32 * D + 32 + r32] * wgt;
-      const float4 x0 = *reinterpret_cast<const float4*>(rec + r32 * D + fg * 8);
-      const float4 x1 = *reinterpret_cast<const float4*>(rec + r32 * D + fg * 8 + 4);
-      acc[0] += x0.x * wgt, acc[1] += x0.y * wgt, acc[2] += x0.z * wgt, acc[3] += x0.w * wgt;
-      acc[4] += x1.x * wgt, acc[5] += x1.y * wgt, acc[6] += x1.z * wgt, acc[7] += x1.w * wgt;
-    }
-    const float invL = 1.0f / L;
-    const int tj = row / a.G, tg = row % a.G;
-    uint16_t* out = a.out + (b * a.block + tj) * a.out_stride0 +
-                    (int64_t)(kh * a.G + tg) * a.out_stride1 + fg * 8;
-    uint32_t w4[4];
+  const int r32 = rgrp * RPW + tid / (P * FG);
+  const int row = rtile * 32 + r32;
+  float M = -INFINITY, L = 0.0f;
+  float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+  for (int s = part; s < nsp; s += P) {
+    const float* rec = base + s * REC;
+    const float ms = rec[32 * D + r32];
+    const float ls = rec[32 * D + 32 + r32];
+    const float4 x0 = *reinterpret_cast<const float4*>(rec + r32 * D + fg * 8);
+    const float4 x1 = *reinterpret_cast<const float4*>(rec + r32 * D + fg * 8 + 4);
+    const float mn = fmaxf(M, ms);
+    const float wa = M == -INFINITY ? 0.0f : exp2f(M - mn);   // rescale what is merged
+    const float wb = ms == -INFINITY ? 0.0f : exp2f(ms - mn);  // weight of this split
+    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    L = L * wa + ls * wb;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w4[e] = (uint32_t)E::from_f(acc[2 * e] * invL) |
-              ((uint32_t)E::from_f(acc[2 * e + 1] * invL) << 16);
-    *reinterpret_cast<uint4*>(out) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    for (int e = 0; e < 8; ++e) acc[e] = acc[e] * wa + xs[e] * wb;
+    M = mn;
   }
+  // combine the P partial merges (lanes part = 0..P-1 are adjacent)
+#pragma unroll
+  for (int mask = 1; mask < P; mask <<= 1) {
+    const float Mo = __shfl_xor(M, mask);
+    const float Lo = __shfl_xor(L, mask);
+    const float mn = fmaxf(M, Mo);
+    const float wa = M == -INFINITY ? 0.0f : exp2f(M - mn);
+    const float wb = Mo == -INFINITY ? 0.0f : exp2f(Mo - mn);
+    L = L * wa + Lo * wb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = acc[e] * wa + __shfl_xor(acc[e], mask) * wb;
+    M = mn;
+  }
+  if (part != 0 || row >= a.M) return;
+  const float invL = 1.0f / L;
+  const int tj = row / a.G, tg = row % a.G;
+  uint16_t* out = a.out + (b * a.block + tj) * a.out_stride0 +
+                  (int64_t)(kh * a.G + tg) * a.out_stride1 + fg * 8;
+  uint32_t w4[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    w4[e] = (uint32_t)E::from_f(acc[2 * e] * invL) |
+            ((uint32_t)E::from_f(acc[2 * e + 1] * invL) << 16);
+  *reinterpret_cast<uint4*>(out) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
 }
 
 template <bool FP16, int D>
 hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   const int64_t g1 = (int64_t)a.B * a.nhk * a.row_tiles * (a.n_splits + 1);
-  const int64_t g2 = (int64_t)a.B * a.nhk * a.row_tiles;
-  if (g1 > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const int64_t g2 = (int64_t)a.B * a.nhk * a.row_tiles * (32 / (256 / (kMergeParts * (D / 8))));
+  if (g1 > 0x7FFFFFFF || g2 > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL((draft_attn_stage1<FP16, D>), dim3((uint32_t)g1), dim3(64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
