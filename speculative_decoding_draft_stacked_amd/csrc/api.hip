@@ -560,10 +560,11 @@ struct AttnPlan {
   int64_t bytes = 0;
 };
 
-// Key splits: enough waves for about 4 per compute unit, each split a
+// Key splits: enough waves for about 4 per compute unit at head_dim 128 and 8
+// at 64 (a step of a 64-wide head requests half the lines), each split a
 // multiple of 32 keys and at least 256 (fewer, longer splits when the batch
-// alone fills the device). Four long waves keep a CU's L1 request queue as
-// full as eight shorter ones, with half the split records to merge.
+// alone fills the device). That keeps a CU's L1 request queue about full;
+// more, shorter splits only add records to merge.
 AttnPlan attn_plan(int64_t B, int32_t block, int32_t nhq, int32_t nhk, int32_t D,
                    int64_t max_prefix, int num_cus) {
   AttnPlan pl;
@@ -571,7 +572,7 @@ AttnPlan attn_plan(int64_t B, int32_t block, int32_t nhq, int32_t nhk, int32_t D
   pl.row_tiles = (int32_t)((M + 31) / 32);
   const int64_t base = B * nhk * pl.row_tiles;
   if (max_prefix > 0) {
-    const int64_t target = 4LL * (num_cus > 0 ? num_cus : 1);
+    const int64_t target = (D <= 64 ? 8LL : 4LL) * (num_cus > 0 ? num_cus : 1);
     int64_t ns = base > 0 ? (target + base - 1) / base : 1;
     if (ns < 1) ns = 1;
     int64_t len = (max_prefix + ns - 1) / ns;
