@@ -451,7 +451,12 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
 // valid row j goes to token split j % splits, tile slot j / splits: the splits
 // share the valid rows evenly without the host knowing their count. Every
 // workgroup runs the same scan (T is small on this path). map[slot] = row, or
-// -1 where the slot holds none; returns this split's number of rows.
+// -1 where the slot holds none; returns this split's number of rows. The scan
+// costs every workgroup a pass per 512 rows, so longer windows (up to 32768
+// rows reach this kernel when there are few weight tiles) keep contiguous
+// splits instead.
+constexpr int64_t kCompactMaxRows = 1024;
+
 template <int BT>
 __device__ int compact_rows(const WriteArgs& a, int64_t sp, int splits, int* map, int* wcnt,
                             int tid) {
@@ -600,7 +605,14 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
   if constexpr (COMMIT) {
 #pragma unroll
     for (int g = 0; g < LOOK; ++g) issue_w(g, wq[g]);
-    const int mine = compact_rows<BT>(a, sp, splits, rmap, wcnt, tid);
+    int mine;
+    if (T <= kCompactMaxRows) {
+      mine = compact_rows<BT>(a, sp, splits, rmap, wcnt, tid);
+    } else {  // the split's contiguous rows; the epilogue applies the window
+      for (int i = tid; i < BT; i += NT) rmap[i] = t0 + i < T ? (int)(t0 + i) : -1;
+      __syncthreads();
+      mine = (int)(T - t0 < BT ? T - t0 : BT);
+    }
     nbe = (mine + 31) / 32;
     if (mine == 0) {  // uniform: nothing of this split is written
       wait_vmcnt<0>();

@@ -207,8 +207,10 @@ def test_commit_len_edges():
 def test_commit_rows_spread_over_token_splits():
     """Small-T commit windows: only written rows are projected, numbered in row
     order and dealt to the token splits in turn. Eight splits with three rows
-    (five splits get none), no rows at all, and a 1600-row window list (50
-    splits, several passes of the row scan) with holes and negative slots."""
+    (five splits get none), no rows at all, a 1000-row window list (32
+    splits, two passes of the row scan) with holes and negative slots, and a
+    1600-row one, past the scan's limit (contiguous splits, the window applied
+    at the store)."""
     case = W.make_case(T=256, H=128, L=2, NH=1, D=64, row_width=8, slots=300, seed=31)
     case.commit_lens = np.zeros(32, dtype=np.int64)
     case.commit_lens[5] = 3
@@ -217,6 +219,9 @@ def test_commit_rows_spread_over_token_splits():
     case.commit_lens[5] = 0
     dc, _, _ = _run(case, "no committed rows")
     assert len(dc.touched_slots(1, "v")) == 0
+    mid = W.make_case(T=1000, H=192, L=1, NH=1, D=64, row_width=8, commit_range=(0, 9),
+                      neg_loc_frac=0.1, slots=1200, seed=33)
+    _run(mid, "1000 rows, 32 splits")
     big = W.make_case(T=1600, H=192, L=1, NH=1, D=64, row_width=8, commit_range=(0, 9),
                       neg_loc_frac=0.1, slots=2000, seed=32)
     _run(big, "1600 rows, 50 splits")
