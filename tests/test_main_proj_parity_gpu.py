@@ -96,9 +96,14 @@ SMALL = {
     # tiled kernel with an odd number of 128-row tiles (the last 256-row
     # workgroup tile is half past the weight)
     "tiled_odd_groups": dict(T=5000, H=1152, n_aux=1),
-    # K split over workgroups (on 256 compute units): 7 weight tiles x 2 token
-    # tiles x 5 K parts of 8 or 9 chunks, ragged token tail
-    "split_odd_parts": dict(T=200, H=896, n_aux=3),
+    # K split over workgroups (on 256 compute units): 12 weight tiles x 2 token
+    # tiles x 9 K parts of 8 chunks, ragged token tail
+    "split_odd_parts": dict(T=200, H=1536, n_aux=3),
+    # hidden size not a multiple of 512: no K split (streaming kernel, 7 tiles)
+    "nosplit_h896": dict(T=200, H=896, n_aux=3),
+    # the largest hidden size of the K-split norm (a row of 8192 in registers,
+    # 4 waves x 4 passes of 512): 64 tiles x 1 token tile x 4 K parts
+    "split_max_h8192": dict(T=64, H=8192, n_aux=1),
     # K split, fp16 with an fp32 norm weight: 4 tiles x 1 token tile x 4 parts
     "split_fp16": dict(T=128, H=512, n_aux=4, dtype="fp16", g_fp32=True),
 }

@@ -227,6 +227,17 @@ def test_commit_rows_spread_over_token_splits():
     _run(big, "1600 rows, 50 splits")
 
 
+@pytest.mark.parametrize("T,row_width", [(70, 7), (3000, None)])
+def test_max_layers(T, row_width):
+    """DSPARK_MAX_LAYERS layers in one pack: every layer's pool descriptor
+    travels in the kernel arguments (streaming path with a commit window, and
+    the tiled path)."""
+    kw = dict(row_width=row_width, commit_range=(0, 8)) if row_width else {}
+    case = W.make_case(T=T, H=128, L=dk.MAX_LAYERS, NH=1, D=64, slots=T + 50, seed=34 + T, **kw)
+    rows = None if T < 1000 else _sample_rows(case, 256, 6)
+    _run(case, f"{dk.MAX_LAYERS} layers, T={T}", rows)
+
+
 def test_all_rows_skipped_and_empty():
     case = W.make_case(T=16, H=64, L=1, NH=1, D=64, slots=32, seed=27)
     case.locs[:] = -1
