@@ -75,7 +75,7 @@ __device__ __forceinline__ uint4 ld16(const uint16_t* p) {
 }
 
 template <bool FP16, int D>
-__global__ __launch_bounds__(64) void draft_attn_stage1(const AttnArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void draft_attn_stage1(const AttnArgs a) {
   using E = AE<FP16>;
   using vec8 = typename E::vec8;
   constexpr int DS = D / 16;          // MFMA steps over the head dimension
@@ -145,33 +145,42 @@ __global__ __launch_bounds__(64) void draft_attn_stage1(const AttnArgs a) {
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
 
   // Keys go in windows of 8 steps of 32: the window's slot indices are loaded
-  // at once, and each step's K and V gathers are issued one step ahead into
-  // alternating registers, so the gathers overlap the previous step's math.
+  // at once, and each step's K and V gathers are issued during the previous
+  // step (see load_k / load_v below), so they overlap its math.
   constexpr int WSTEPS = 8;
   // K and V are gathered alike: lane (key r32, half h) takes features
   // 16s + 8h + [0, 8) of its key's row, which is the MFMA A layout for K and,
   // written to the transposed tile, puts 32 consecutive keys of one feature
   // row in one instruction (no bank conflicts between the 16-lane groups).
-  uint4 kf[2][DS], vu[2][DS];
-  auto load_kv = [&](int64_t krow, uint4(&kd)[DS], uint4(&vd)[DS]) {
+  // One register buffer each for K and V: the next step's K rows are
+  // gathered as soon as this step's S MFMAs have read the current ones, and
+  // its V rows once the current ones are in the LDS tile, so both stay one
+  // step ahead with half the registers of a double buffer. With that the
+  // kernel fits 256 registers, two waves per SIMD at head_dim 128, so the
+  // block-key waves run alongside the prefix splits instead of after them.
+  uint4 kf[DS], vu[DS];
+  auto load_k = [&](int64_t krow) {
 #pragma unroll
-    for (int s = 0; s < DS; ++s) kd[s] = ld16(kbase + krow + 16 * s + 8 * hh);
-#pragma unroll
-    for (int s = 0; s < DS; ++s) vd[s] = ld16(vbase + krow + 16 * s + 8 * hh);
+    for (int s = 0; s < DS; ++s) kf[s] = ld16(kbase + krow + 16 * s + 8 * hh);
   };
-  auto step = [&](const uint4(&kd)[DS], const uint4(&vd)[DS], unsigned long long vmask) {
+  auto load_v = [&](int64_t krow) {
+#pragma unroll
+    for (int s = 0; s < DS; ++s) vu[s] = ld16(vbase + krow + 16 * s + 8 * hh);
+  };
+  auto step = [&](unsigned long long vmask, bool more, int64_t knext) {
     // S^T = K * Q^T over the head dimension
     f32x16 st;
 #pragma unroll
     for (int r = 0; r < 16; ++r) st[r] = 0.0f;
 #pragma unroll
-    for (int s = 0; s < DS; ++s) st = E::mfma(__builtin_bit_cast(vec8, kd[s]), qf[s], st);
+    for (int s = 0; s < DS; ++s) st = E::mfma(__builtin_bit_cast(vec8, kf[s]), qf[s], st);
+    if (more) load_k(knext);  // uniform
 
     // V^T tile into LDS: vt[d][key], zero rows for masked keys
     const bool vok = (vmask >> r32) & 1ull;
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
-      const uint4 u = vok ? vd[s] : make_uint4(0, 0, 0, 0);
+      const uint4 u = vok ? vu[s] : make_uint4(0, 0, 0, 0);
       const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
       uint16_t* col = vt + (16 * s + 8 * hh) * KS + r32;
 #pragma unroll
@@ -180,6 +189,7 @@ __global__ __launch_bounds__(64) void draft_attn_stage1(const AttnArgs a) {
         col[(2 * e + 1) * KS] = (uint16_t)(w4[e] >> 16);
       }
     }
+    if (more) load_v(knext);
 
     // online softmax of this lane's row over the 32 keys (16 here, 16 in lane ^ 32)
     float sv[16];
@@ -249,12 +259,14 @@ __global__ __launch_bounds__(64) void draft_attn_stage1(const AttnArgs a) {
       }
       vmask[j] = __ballot(kvalid);
     }
-    load_kv(krow[0], kf[0], vu[0]);
+    load_k(krow[0]);
+    load_v(krow[0]);
 #pragma unroll
     for (int j = 0; j < WSTEPS; ++j) {
-      if (j + 1 < WSTEPS && w0 + 32 * (j + 1) < kend)  // uniform over the wave
-        load_kv(krow[j + 1], kf[(j + 1) & 1], vu[(j + 1) & 1]);
-      if (w0 + 32 * j < kend) step(kf[j & 1], vu[j & 1], vmask[j]);
+      if (w0 + 32 * j < kend) {  // uniform over the wave
+        const bool more = j + 1 < WSTEPS && w0 + 32 * (j + 1) < kend;
+        step(vmask[j], more, more ? krow[j + 1] : 0);
+      }
     }
   }
 
