@@ -25,8 +25,8 @@
 //     lane-local.
 //   The split leaves fp32 (O, m, l) per row in the workspace.
 // Stage 2: per row, M = max m, L = sum l * 2^(m - M), O = sum O * 2^(m - M) / L,
-// rounded once to the dtype; four threads per (row, 8 features), each merging a
-// quarter of the splits. Keys past a request's prefix, and slots outside the
+// rounded once to the dtype; 4 or 8 threads per (row, 8 features), each
+// merging a share of the splits. Keys past a request's prefix, and slots outside the
 // pool (counted), are masked with a zero value row.
 #include "internal.h"
 
@@ -285,20 +285,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void dr
   }
 }
 
-// Stage 2: four threads per (row, 8 features) of a (request, KV head, row
-// tile) record, each merging every fourth split online (running max M, sum L
-// and weighted O, rescaled as each split arrives, so its loads of all its
-// splits are independent and go out together); the four partial merges are
-// then combined by two lane swaps in a fixed order. An empty split has m =
-// -inf, l = 0 and O = 0 and adds nothing. A workgroup takes 256 / (4 * D / 8)
-// rows of a record, so short records still spread over many workgroups.
-constexpr int kMergeParts = 4;
+// Stage 2: P threads per (row, 8 features) of a (request, KV head, row tile)
+// record (P = 4 at head_dim 128, 8 at 64, where records have twice the
+// splits), each merging every P-th split online (running max M, sum L and
+// weighted O, rescaled as each split arrives, so its loads of all its splits
+// are independent and go out together); the P partial merges are then
+// combined by lane swaps in a fixed order. An empty split has m = -inf, l = 0
+// and O = 0 and adds nothing. A workgroup takes 256 / (P * D / 8) rows of a
+// record, so short records still spread over many workgroups.
+template <int D>
+constexpr int kMergeParts = D <= 64 ? 8 : 4;
 
 template <bool FP16, int D>
 __global__ __launch_bounds__(256) void draft_attn_stage2(const AttnArgs a) {
   using E = AE<FP16>;
   constexpr int FG = D / 8;                     // 8-feature groups of a row
-  constexpr int P = kMergeParts;
+  constexpr int P = kMergeParts<D>;
   constexpr int RPW = 256 / (P * FG);           // rows per workgroup
   constexpr int64_t REC = 32 * (D + 2);
   static_assert(32 % RPW == 0, "row groups tile the 32-row record");
@@ -363,7 +365,7 @@ __global__ __launch_bounds__(256) void draft_attn_stage2(const AttnArgs a) {
 template <bool FP16, int D>
 hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   const int64_t g1 = (int64_t)a.B * a.nhk * a.row_tiles * (a.n_splits + 1);
-  const int64_t g2 = (int64_t)a.B * a.nhk * a.row_tiles * (32 / (256 / (kMergeParts * (D / 8))));
+  const int64_t g2 = (int64_t)a.B * a.nhk * a.row_tiles * (32 / (256 / (kMergeParts<D> * (D / 8))));
   if (g1 > 0x7FFFFFFF || g2 > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL((draft_attn_stage1<FP16, D>), dim3((uint32_t)g1), dim3(64), 0, stream, a);
   hipError_t e = hipGetLastError();
