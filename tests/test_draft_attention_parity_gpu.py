@@ -160,3 +160,28 @@ def test_graph_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(d.host(), ref), rep
+
+
+def _draw_attn(i):
+    rng = np.random.default_rng(9500 + i)
+    nhk = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    B = int(rng.integers(1, 13))
+    prefix = [int(x) for x in rng.integers(0, 3000, size=B)]
+    if rng.random() < 0.3:
+        prefix[int(rng.integers(0, B))] = 0
+    return dict(name=f"attn_sweep{i}", B=B, block=int(rng.integers(1, 49)), nhq=nhk * G, nhk=nhk,
+                D=int(rng.choice([64, 128])), prefix=prefix,
+                slots=sum(prefix) + int(rng.integers(1, 100)),
+                dtype="fp16" if rng.random() < 0.3 else "bf16", seed=9500 + i)
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_shapes(i):
+    """Seeded sweep: request count, block length (1..48 own keys), grouping
+    (1..8 query heads per KV head, so 1..12 row tiles), head_dim, prefix
+    lengths 0..2999 and dtype drawn per case; every request checked."""
+    kw = _draw_attn(i)
+    c = W.make_attn_case(**kw)
+    d, _ = _run(c, kw["name"])
+    assert int(d.err.item()) == 0

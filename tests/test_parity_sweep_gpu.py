@@ -1,0 +1,77 @@
+"""Seeded sweep of random shapes through the HIP context-KV write (C ABI)
+against the CPU oracle, to the same bar as the named cases: the written
+(layer, slot) set bit-exact, values within (2e-2, 2e-2) for bf16 and
+(5e-3, 5e-3) for fp16.
+
+Each case draws T, H, L, KV heads, head_dim, dtype, bias, and the slot map
+(plain slots with holes, or commit windows with lengths 0..W+2) from one
+seed, so the sweep crosses both kernels, their tile and token-split choices,
+K tails, commit-window compaction and its limit. Sizes keep the fp64 oracle
+to about a second per case.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import speculative_decoding_draft_stacked_amd as dk
+from speculative_decoding_draft_stacked_amd import workloads as W
+
+from gpu_util import DeviceCase, check_slot_sets, compare_rows, say
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 40
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "no GPU visible"
+    dk.lib()  # raises if the HIP library is not built
+
+
+def _draw(i):
+    rng = np.random.default_rng(9000 + i)
+    D = int(rng.choice([64, 128]))
+    NH = int(rng.integers(1, 5))
+    L = int(rng.integers(1, 7))
+    H = int(rng.integers(1, 129)) * 8
+    n_tot = L * 2 * NH * D
+    dtype = "fp16" if rng.random() < 0.3 else "bf16"
+    bias = bool(rng.random() < 0.3)
+    # T: mostly decode-sized, some large enough for the tiled kernel
+    T = int(rng.integers(1, 300)) if rng.random() < 0.5 else int(rng.integers(1000, 9000))
+    # keep T * n_tot * H (the oracle's work) near or under 4e9
+    while T > 1 and T * n_tot * H > 4e9:
+        T = T * 2 // 3
+    kw = dict(name=f"sweep{i}", T=T, H=H, L=L, NH=NH, D=D, dtype=dtype, bias=bias,
+              seed=9000 + i, theta=float(rng.choice([1e4, 5e4, 1e6])), P=4096)
+    if rng.random() < 0.5:
+        Wd = int(rng.integers(1, 17))
+        T = max(Wd, T // Wd * Wd)
+        kw.update(T=T, row_width=Wd, commit_range=(0, Wd + 2))
+    kw["neg_loc_frac"] = float(rng.choice([0.0, 0.0, 0.1]))
+    kw["slots"] = T + int(rng.integers(0, 64))
+    return kw
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_shape(i):
+    kw = _draw(i)
+    case = W.make_case(**kw)
+    say(f"[sweep {i}] T={case.T} H={case.H} L={case.L} NH={case.NH} D={case.D} {case.dtype} "
+        f"bias={case.qkv_b is not None} W={case.row_width}")
+    dc = DeviceCase(case)
+    pack = dc.pack()
+    assert dc.write(pack)
+    torch.cuda.synchronize()
+    check_slot_sets(dc)
+    rows = None
+    if case.T > 1500:
+        rng = np.random.default_rng(i)
+        rows = np.unique(np.concatenate([rng.choice(case.T, 400, replace=False),
+                                         [0, case.T - 1]]))
+    st = compare_rows(dc, rows, f"sweep{i}")
+    assert pack.range_errors() == 0
+    say(f"  ok: {st}")
+    pack.free()
