@@ -26,6 +26,9 @@ struct dspark_ctx_kv_pack {
   int64_t table_rows;
   unsigned long long* err;   // range error counter
   uint16_t* zeros;           // 256 zero bytes read by out-of-range K lanes
+  float* part;               // K-split workspace of the write (part_cap floats) or nullptr
+  int64_t part_cap;
+  int* rowmap;               // committed-row map of the K-split form
 };
 
 namespace {
@@ -48,6 +51,8 @@ void free_pack(dspark_ctx_kv_pack* p) {
   if (p->knw) (void)hipFree(p->knw);
   if (p->err) (void)hipFree(p->err);
   if (p->zeros) (void)hipFree(p->zeros);
+  if (p->part) (void)hipFree(p->part);
+  if (p->rowmap) (void)hipFree(p->rowmap);
   delete p;
 }
 
@@ -145,6 +150,14 @@ int dspark_pack_ctx_kv(const dspark_layer_desc* layers, int32_t num_layers, int6
   if (hipMalloc(&p->err, sizeof(unsigned long long)) != hipSuccess) return fail(DSPARK_E_NOMEM);
   if (hipMalloc(&p->zeros, 256) != hipSuccess) return fail(DSPARK_E_NOMEM);
   if (hipMalloc(&differ, sizeof(int)) != hipSuccess) return fail(DSPARK_E_NOMEM);
+  // workspace of the write's K-split form, used when the weight has few
+  // 128-row tiles for the device (at most one workgroup per compute unit)
+  if (n_tot / 128 * 2 <= p->num_cus) {
+    p->part_cap = (int64_t)p->num_cus * dspark::kPartFloatsPerCU;
+    if (hipMalloc(&p->part, (size_t)p->part_cap * 4) != hipSuccess ||
+        hipMalloc(&p->rowmap, dspark::kRowMapInts * sizeof(int)) != hipSuccess)
+      return fail(DSPARK_E_NOMEM);
+  }
 
   bool ok = true;
   for (int32_t l = 0; l < num_layers && ok; ++l) {
@@ -230,6 +243,9 @@ int dspark_ctx_kv_write(const dspark_ctx_kv_pack* p, const void* ctx_hidden, int
   a.bias = p->bias;
   a.knw = p->knw;
   a.zeros = p->zeros;
+  a.partial = p->part;
+  a.rowmap = p->rowmap;
+  a.part_cap = p->part_cap;
   a.table = p->table;
   a.pos = positions;
   a.locs = locs;

@@ -556,10 +556,11 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
   // Workgroup b runs on XCD b % 8. When the row tiles divide evenly, the
   // `splits` workgroups sharing a weight tile are placed on one XCD and
   // dispatched back to back, so its L2 serves the tile to all of them.
-  // The producer may also split K over workgroups (a.ksplits > 1): workgroup
-  // b takes K part b / (R * splits) and writes fp32 partial sums instead of
-  // the epilogue; the row-norm kernel adds the parts.
-  const int ks = (D == kRowsOut && a.ksplits > 1) ? a.ksplits : 1;
+  // K may also be split over workgroups (a.ksplits > 1): workgroup b takes K
+  // part b / (R * splits) and writes fp32 partial sums instead of the
+  // epilogue; the producer's row-norm kernel, or ctx_kv_stream_reduce for the
+  // write, adds the parts.
+  const int ks = a.ksplits > 1 ? a.ksplits : 1;
   const int64_t kq = (int64_t)blockIdx.x / (R * splits);
   const int64_t b = (int64_t)blockIdx.x % (R * splits);
   int64_t rt, sp;
@@ -624,6 +625,8 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
       mine = (int)(T - t0 < BT ? T - t0 : BT);
     }
     nbe = (mine + 31) / 32;
+    if (D != kRowsOut && ks > 1 && kq == 0 && rt == 0)  // for ctx_kv_stream_reduce
+      for (int i = tid; i < BT; i += NT) a.rowmap[sp * BT + i] = rmap[i];
     if (mine == 0) {  // uniform: nothing of this split is written
       wait_vmcnt<0>();
       return;
@@ -718,6 +721,29 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
       }
   }
   __syncthreads();
+  if (D != kRowsOut && ks > 1) {
+    // fp32 sums of this K part in the MFMA accumulator layout: tile (kq, rt,
+    // sp) of BT x 128 floats, (block tb, row group w, quad q) 256 floats at
+    // ((tb * 4 + w) * 4 + q) * 256, lane l at 4 l (one KiB per store)
+    if (par == 0) {
+      float* part = a.partial + ((int64_t)kq * R * splits + rt * splits + sp) * (int64_t)(BT * BN) +
+                    w * 1024 + lane * 4;
+#pragma unroll
+      for (int tb = 0; tb < NB; ++tb) {
+        if (tb >= nbe) break;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int tok = tb * 32 + r32;
+          const int row = 32 * w + 8 * q + 4 * hh;
+          const float4 o = *reinterpret_cast<const float4*>(red + tok * RS + row);
+          *reinterpret_cast<float4*>(part + tb * 4096 + q * 256) =
+              make_float4(acc[tb][4 * q] + o.x, acc[tb][4 * q + 1] + o.y,
+                          acc[tb][4 * q + 2] + o.z, acc[tb][4 * q + 3] + o.w);
+        }
+      }
+    }
+    return;
+  }
   if (D == kRowsOut && ks > 1) {
     // fp32 partial sums of this K part: partial[(kq * T + t) * (R * 128) + n]
     if (par == 0) {
@@ -765,6 +791,76 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
     scatter_tile<E, D, BT, COMMIT, LDO, NT>(a, sO, n0, t0, tid, COMMIT ? rmap : nullptr);
 }
 
+// Second launch of the write's K-split form: workgroup (rt, sp) adds the K
+// parts of its tile in part order (so the sums do not depend on timing), adds
+// the bias, rounds to the dtype and runs the epilogue of ctx_kv_stream_kernel
+// for the tile's rows (the committed-row map comes from K part 0's workgroup
+// of row tile 0).
+template <bool FP16, int D, bool BIAS, bool COMMIT, int NB>
+__global__ __launch_bounds__(512) void ctx_kv_stream_reduce(const WriteArgs a, int splits) {
+  using E = Elem<FP16>;
+  constexpr int NT = 512;
+  constexpr int BT = 32 * NB;
+  constexpr int LDO = BN + 4;
+  __shared__ __align__(16) uint16_t sO[BT * LDO];
+  __shared__ int smap[BT];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r32 = lane & 31;
+  const int hh = lane >> 5;
+  const int64_t R = a.R;
+  const int64_t rt = blockIdx.x / splits;
+  const int64_t sp = blockIdx.x % splits;
+  const int ks = a.ksplits;
+  if (COMMIT)
+    for (int i = tid; i < BT; i += NT) smap[i] = a.rowmap[sp * BT + i];
+  const int64_t pstride = R * splits * (int64_t)(BT * BN);  // floats between K parts
+  const float* src0 = a.partial + (rt * splits + sp) * (int64_t)(BT * BN);
+  // 8 waves: wave = (row group w, half of the token blocks)
+  const int w = wave & 3;
+  for (int tb = wave >> 2; tb < NB; tb += 2) {
+    const float* src = src0 + tb * 4096 + w * 1024 + lane * 4;
+    float4 sum[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sum[q] = *reinterpret_cast<const float4*>(src + q * 256);
+    for (int k0 = 1; k0 < ks; k0 += 4) {  // up to four parts' loads in flight, added in order
+      float4 v[4][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (k0 + u < ks) v[u][q] = *reinterpret_cast<const float4*>(src + (k0 + u) * pstride + q * 256);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (k0 + u < ks) {
+            sum[q].x += v[u][q].x;
+            sum[q].y += v[u][q].y;
+            sum[q].z += v[u][q].z;
+            sum[q].w += v[u][q].w;
+          }
+    }
+    const int tok = tb * 32 + r32;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = 32 * w + 8 * q + 4 * hh;
+      float v[4] = {sum[q].x, sum[q].y, sum[q].z, sum[q].w};
+      if (BIAS) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] += E::to_f(a.bias[rt * BN + row + i]);
+      }
+      uint2 packed;
+      packed.x = E::from_f(v[0]) | (E::from_f(v[1]) << 16);
+      packed.y = E::from_f(v[2]) | (E::from_f(v[3]) << 16);
+      *reinterpret_cast<uint2*>(sO + tok * LDO + row) = packed;
+    }
+  }
+  __syncthreads();
+  scatter_tile<E, D, BT, COMMIT, LDO, NT>(a, sO, rt * BN, sp * BT, tid, COMMIT ? smap : nullptr);
+}
+
 template <bool FP16, int D, bool BIAS, bool COMMIT, int BT>
 hipError_t launch_tiled_bt(const WriteArgs& a, int64_t grid, int64_t t_tiles, hipStream_t stream) {
   hipLaunchKernelGGL((ctx_kv_tiled_kernel<FP16, D, BIAS, COMMIT, BT>), dim3((uint32_t)grid),
@@ -796,8 +892,42 @@ hipError_t launch_tiled(const WriteArgs& a, int num_cus, hipStream_t stream) {
   }
 }
 
+// K parts for the write's streaming kernel: where its row tiles x token
+// splits leave at least half of the device idle (few weight tiles, e.g. one
+// GPU's share of the KV heads), K is split over workgroups too, so that the
+// grid fills the device and each workgroup streams a slice of its tile; the
+// fp32 part sums then cost a second launch (ctx_kv_stream_reduce). 1: none.
+constexpr int64_t kKSplitTokenSplits = 4;
+
+int write_ksplits(const WriteArgs& a, int64_t row_tiles, int64_t splits, int nb, int num_cus) {
+  if (a.part_cap <= 0 || !a.partial || !a.rowmap || a.T > kCompactMaxRows) return 1;
+  if (row_tiles * splits * 2 > num_cus) return 1;
+  const int64_t nk_all = (a.H + BK - 1) / BK;
+  int64_t ks = num_cus / (row_tiles * splits);
+  if (ks > nk_all / 8) ks = nk_all / 8;  // at least 8 chunks of 64 per part
+  if (ks > 16) ks = 16;
+  if (ks < 2 || splits * 32 * nb > kRowMapInts ||
+      ks * row_tiles * splits * 32 * nb * BN > a.part_cap)
+    return 1;
+  return (int)ks;
+}
+
 template <bool FP16, int D, bool BIAS, bool COMMIT, int NB>
-hipError_t launch_stream_nb(const WriteArgs& a, int64_t row_tiles, int splits, hipStream_t stream) {
+hipError_t launch_stream_nb(const WriteArgs& a, int64_t row_tiles, int splits, int num_cus,
+                            hipStream_t stream) {
+  const int ks = D == kRowsOut ? 1 : write_ksplits(a, row_tiles, splits, NB, num_cus);
+  if (ks > 1) {
+    WriteArgs b = a;
+    b.ksplits = ks;
+    hipLaunchKernelGGL((ctx_kv_stream_kernel<FP16, D, BIAS, COMMIT, NB>),
+                       dim3((uint32_t)(row_tiles * splits * ks)), dim3(512), 0, stream, b, splits);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if constexpr (D != kRowsOut)
+      hipLaunchKernelGGL((ctx_kv_stream_reduce<FP16, D, BIAS, COMMIT, NB>),
+                         dim3((uint32_t)(row_tiles * splits)), dim3(512), 0, stream, b, splits);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((ctx_kv_stream_kernel<FP16, D, BIAS, COMMIT, NB>),
                      dim3((uint32_t)(row_tiles * splits)), dim3(512), 0, stream, a, splits);
   return hipGetLastError();
@@ -812,13 +942,22 @@ hipError_t launch_by_rows(const WriteArgs& a, int num_cus, hipStream_t stream) {
   const int64_t cap = row_tiles >= num_cus ? 1 : num_cus / row_tiles;
   if (blocks > 4 * cap) return launch_tiled<FP16, D, BIAS, COMMIT>(a, num_cus, stream);
   int64_t splits = blocks < cap ? blocks : cap;
-  const int64_t nb = (blocks + splits - 1) / splits;
+  int64_t nb = (blocks + splits - 1) / splits;
   splits = (blocks + nb - 1) / nb;
+  // With K split over workgroups as well, fewer token splits (each weight
+  // line requested by fewer workgroups) and more K parts cost less: at most
+  // kKSplitTokenSplits splits of up to 4 blocks.
+  if (D != kRowsOut && splits > kKSplitTokenSplits &&
+      write_ksplits(a, row_tiles, splits, (int)nb, num_cus) > 1) {
+    const int64_t s2 = (blocks + 3) / 4 > kKSplitTokenSplits ? (blocks + 3) / 4 : kKSplitTokenSplits;
+    nb = (blocks + s2 - 1) / s2;
+    splits = (blocks + nb - 1) / nb;
+  }
   switch (nb) {
-    case 1: return launch_stream_nb<FP16, D, BIAS, COMMIT, 1>(a, row_tiles, (int)splits, stream);
-    case 2: return launch_stream_nb<FP16, D, BIAS, COMMIT, 2>(a, row_tiles, (int)splits, stream);
-    case 3: return launch_stream_nb<FP16, D, BIAS, COMMIT, 3>(a, row_tiles, (int)splits, stream);
-    default: return launch_stream_nb<FP16, D, BIAS, COMMIT, 4>(a, row_tiles, (int)splits, stream);
+    case 1: return launch_stream_nb<FP16, D, BIAS, COMMIT, 1>(a, row_tiles, (int)splits, num_cus, stream);
+    case 2: return launch_stream_nb<FP16, D, BIAS, COMMIT, 2>(a, row_tiles, (int)splits, num_cus, stream);
+    case 3: return launch_stream_nb<FP16, D, BIAS, COMMIT, 3>(a, row_tiles, (int)splits, num_cus, stream);
+    default: return launch_stream_nb<FP16, D, BIAS, COMMIT, 4>(a, row_tiles, (int)splits, num_cus, stream);
   }
 }
 

@@ -10,6 +10,12 @@ namespace dspark {
 
 constexpr int kMaxLayers = DSPARK_MAX_LAYERS;
 
+// Workspace the pack owns for the write's K-split form (few weight tiles):
+// fp32 part sums of at most one workgroup per compute unit, each at most a
+// 128-row x 128-token tile, and the committed-row map of the token splits.
+constexpr int64_t kPartFloatsPerCU = 128 * 128;
+constexpr int kRowMapInts = 2048;
+
 // Everything the fused write kernel reads, passed by value in the kernel
 // arguments so that one launch can address every layer's pool.
 struct WriteArgs {
@@ -24,10 +30,13 @@ struct WriteArgs {
   const int64_t* commit;    // [T / W] or nullptr
   unsigned long long* err;  // range error counter
   uint16_t* y;              // producer only: [T, R * 128] output rows (row stride y_stride)
-  float* partial;           // producer only: [R, T] sums of squares per 128-feature group
+  float* partial;           // producer: [R, T] sums of squares per 128-feature group;
+                            // write: the pack's fp32 K-part workspace (part_cap floats)
+  int* rowmap;              // write: the pack's committed-row map (kRowMapInts ints)
+  int64_t part_cap;         // write: floats in `partial` (0: no K split)
   int64_t y_stride;
   int64_t R;                // 128-row tiles of the blocked weight
-  int32_t ksplits;          // producer only: K parts over workgroups (<= 1: none)
+  int32_t ksplits;          // K parts over workgroups (<= 1: none); set by the launchers
   int64_t x_stride;
   int64_t T;
   int64_t P;

@@ -174,7 +174,8 @@ def make_case(
     )
 
 
-# The five workloads the context-KV write is measured and checked on.
+# The workloads the context-KV write is measured and checked on: the five
+# configurations, and one GPU's share of decode_commit under KV-head sharding.
 WORKLOADS = {
     # 2 requests x 8 rows, tiny draft: 2 layers, 2 KV heads of 64.
     "tiny": dict(T=16, H=256, L=2, NH=2, D=64, dtype=BF16, theta=1e4, P=4096, slots=64),
@@ -191,8 +192,13 @@ WORKLOADS = {
     # Wide hidden, head_dim 64: 64 requests x 8 columns with commit_lens.
     "wide_gqa_d64": dict(T=512, H=7168, L=5, NH=8, D=64, dtype=BF16, row_width=8, theta=5e4,
                          P=32768, slots=131072),
+    # One GPU's share of decode_commit when the KV heads are split over 8 GPUs
+    # (each GPU packs and writes one KV head of every layer; nothing is exchanged).
+    "decode_commit_kv1": dict(T=256, H=4096, L=5, NH=1, D=128, dtype=BF16, row_width=8,
+                              theta=1e6, P=32768, slots=65536),
 }
-WORKLOAD_ORDER = ["tiny", "decode_commit", "prefill_8k", "biased_fp16", "wide_gqa_d64"]
+WORKLOAD_ORDER = ["tiny", "decode_commit", "prefill_8k", "biased_fp16", "wide_gqa_d64",
+                  "decode_commit_kv1"]
 
 
 def workload(name: str) -> Case:

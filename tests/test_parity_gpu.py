@@ -6,6 +6,7 @@ tolerances of sglang PR #31986's stacked-vs-per-layer test. Which slots are
 written is compared bit-exactly against sentinel-filled pools.
 """
 
+import dataclasses
 import zlib
 
 import numpy as np
@@ -97,7 +98,44 @@ def test_k_norm_weight_fp32_and_padded_pool_rows():
     _run(case, "fp32 k_norm, pool stride0 = NH*D + 16", k_norm_fp32=True, pool_row_pad=16)
 
 
-# ------------------------------------------------------------ the five workloads
+# ------------------------------------------------------------ K split over workgroups
+
+K_SPLIT = {
+    # few weight tiles for the device: K is split over workgroups as well, the
+    # parts are added in order by a second launch before the epilogue
+    "no_commit_7_splits_4_parts": dict(T=200, H=2048, L=2, NH=1, D=128, slots=512),
+    "fp16_d64_bias_commit_2_parts": dict(T=96, H=1024, L=1, NH=2, D=64, dtype="fp16", bias=True,
+                                         row_width=6, commit_range=(0, 7), neg_loc_frac=0.1,
+                                         slots=256),
+    "window_1024_32_splits": dict(T=1024, H=4096, L=1, NH=1, D=128, row_width=8, slots=2048),
+}
+
+
+@pytest.mark.parametrize("name", sorted(K_SPLIT))
+def test_k_split_form(name):
+    case = W.make_case(name=name, seed=40 + sorted(K_SPLIT).index(name), **K_SPLIT[name])
+    _run(case, name)
+
+
+def test_k_split_second_call_same_pack():
+    """The K-part workspace belongs to the pack: a second, smaller call through
+    the same pack (the first 64 rows of the batch, fresh pools) writes what the
+    oracle gives for those rows."""
+    c1 = W.make_case(name="ks1", seed=45, T=200, H=2048, L=2, NH=1, D=128, row_width=8,
+                     slots=512)
+    _, pack, _ = _run(c1, "first call")
+    c2 = dataclasses.replace(c1, name="ks2", T=64, x=c1.x[:64], positions=c1.positions[:64],
+                             locs=c1.locs[:64], commit_lens=c1.commit_lens[:8])
+    dc2 = DeviceCase(c2)
+    say("[case] second call through the first pack: T=64")
+    assert dc2.write(pack)
+    torch.cuda.synchronize()
+    check_slot_sets(dc2)
+    compare_rows(dc2, None, "second call")
+    assert pack.range_errors() == 0
+
+
+# ------------------------------------------------------------ the workloads
 
 def _sample_rows(case, n, seed):
     rng = np.random.default_rng(seed)
@@ -107,7 +145,7 @@ def _sample_rows(case, n, seed):
 
 @pytest.mark.parametrize("name,sample", [
     ("tiny", None), ("decode_commit", None), ("wide_gqa_d64", None), ("biased_fp16", 768),
-    ("prefill_8k", 384)])
+    ("prefill_8k", 384), ("decode_commit_kv1", None)])
 def test_workload(name, sample):
     case = W.workload(name)
     rows = None if sample is None else _sample_rows(case, sample, 5)
