@@ -130,7 +130,10 @@ int dspark_check_eligibility(const dspark_layer_desc* layers, int32_t num_layers
  * tables whose pointers differ, then allocates and fills on `stream`:
  * W_stacked [L*2*kv, hidden] (layer-major, K rows then V rows), the stacked bias
  * [L*2*kv] when present, k_norm [L, head_dim] widened to fp32. The rotary table
- * of layer 0 is referenced, not copied: it must outlive the pack. Synchronises
+ * of layer 0 is referenced, not copied: it must outlive the pack. When the
+ * weight has at most (compute units / 2) 128-row tiles, the pack also
+ * allocates a workspace for the write's K-split form (128 x 128 fp32 per
+ * compute unit, 16 MiB on 256 CUs, and a row map). Synchronises
  * `stream` before returning, so the source weights may change afterwards; the
  * pack then still holds the old values (re-pack after a weight update).
  * Returns DSPARK_OK with *out set, DSPARK_FALLBACK with *fallback_reason set
@@ -154,6 +157,8 @@ int dspark_pack_ctx_kv(const dspark_layer_desc* layers, int32_t num_layers, int6
  *     Without commit_lens, locs_row_width and num_requests must be 0.
  *   pools: host array of num_pools == L descriptors, layer order of the pack.
  * Valid slots must be distinct (the scatter is not ordered between rows).
+ * Writes through one pack may use its workspace: calls that overlap in time
+ * (on different streams) must use different packs.
  * A row whose position is outside [0, rope_max_pos) or whose loc is
  * >= that layer's num_slots is not written and is counted in the pack's range
  * error counter (dspark_pack_range_errors); no memory outside the given
