@@ -561,10 +561,20 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
   // epilogue; the producer's row-norm kernel, or ctx_kv_stream_reduce for the
   // write, adds the parts.
   const int ks = a.ksplits > 1 ? a.ksplits : 1;
-  const int64_t kq = (int64_t)blockIdx.x / (R * splits);
+  int64_t kq = (int64_t)blockIdx.x / (R * splits);
   const int64_t b = (int64_t)blockIdx.x % (R * splits);
   int64_t rt, sp;
-  if (R % 8 == 0) {
+  if (D != kRowsOut && ks > 1) {
+    // the write's K parts: the token splits of one (row tile, K part) slice
+    // are 8 workgroups apart, i.e. on one XCD, whose L2 then fetches the
+    // weight slice once for all of them; the grid is padded to whole groups
+    // of 8 slices
+    const int64_t slice = ((int64_t)blockIdx.x / (8 * splits)) * 8 + blockIdx.x % 8;
+    if (slice >= R * ks) return;  // padding
+    sp = ((int64_t)blockIdx.x / 8) % splits;
+    rt = slice / ks;
+    kq = slice % ks;
+  } else if (R % 8 == 0) {
     const int64_t i = b / 8;
     rt = 8 * (i / splits) + b % 8;
     sp = i % splits;
@@ -791,74 +801,76 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
     scatter_tile<E, D, BT, COMMIT, LDO, NT>(a, sO, n0, t0, tid, COMMIT ? rmap : nullptr);
 }
 
-// Second launch of the write's K-split form: workgroup (rt, sp) adds the K
-// parts of its tile in part order (so the sums do not depend on timing), adds
-// the bias, rounds to the dtype and runs the epilogue of ctx_kv_stream_kernel
-// for the tile's rows (the committed-row map comes from K part 0's workgroup
-// of row tile 0).
+// Second launch of the write's K-split form: workgroup (rt, sp, tb) adds the
+// K parts of one 32-token block of its tile in part order (so the sums do not
+// depend on timing), adds the bias, rounds to the dtype and runs the epilogue
+// of ctx_kv_stream_kernel for those rows (the committed-row map comes from K
+// part 0's workgroup of row tile 0).
 template <bool FP16, int D, bool BIAS, bool COMMIT, int NB>
-__global__ __launch_bounds__(512) void ctx_kv_stream_reduce(const WriteArgs a, int splits) {
+__global__ __launch_bounds__(256) void ctx_kv_stream_reduce(const WriteArgs a, int splits) {
   using E = Elem<FP16>;
-  constexpr int NT = 512;
+  constexpr int NT = 256;
   constexpr int BT = 32 * NB;
   constexpr int LDO = BN + 4;
-  __shared__ __align__(16) uint16_t sO[BT * LDO];
-  __shared__ int smap[BT];
+  __shared__ __align__(16) uint16_t sO[32 * LDO];
+  __shared__ int smap[32];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int w = tid >> 6;  // 32-row group
   const int r32 = lane & 31;
   const int hh = lane >> 5;
   const int64_t R = a.R;
-  const int64_t rt = blockIdx.x / splits;
-  const int64_t sp = blockIdx.x % splits;
+  const int tb = (int)(blockIdx.x % NB);
+  const int64_t sp = (blockIdx.x / NB) % splits;
+  const int64_t rt = blockIdx.x / ((int64_t)NB * splits);
   const int ks = a.ksplits;
-  if (COMMIT)
-    for (int i = tid; i < BT; i += NT) smap[i] = a.rowmap[sp * BT + i];
+  if (COMMIT) {
+    // the split's rows are compacted: a block whose first slot is empty is empty
+    if (a.rowmap[sp * BT + tb * 32] < 0) return;
+    if (tid < 32) smap[tid] = a.rowmap[sp * BT + tb * 32 + tid];
+  } else if (sp * BT + tb * 32 >= a.T) {
+    return;
+  }
   const int64_t pstride = R * splits * (int64_t)(BT * BN);  // floats between K parts
-  const float* src0 = a.partial + (rt * splits + sp) * (int64_t)(BT * BN);
-  // 8 waves: wave = (row group w, half of the token blocks)
-  const int w = wave & 3;
-  for (int tb = wave >> 2; tb < NB; tb += 2) {
-    const float* src = src0 + tb * 4096 + w * 1024 + lane * 4;
-    float4 sum[4];
+  const float* src = a.partial + (rt * splits + sp) * (int64_t)(BT * BN) + tb * 4096 + w * 1024 +
+                     lane * 4;
+  float4 sum[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) sum[q] = *reinterpret_cast<const float4*>(src + q * 256);
-    for (int k0 = 1; k0 < ks; k0 += 4) {  // up to four parts' loads in flight, added in order
-      float4 v[4][4];
+  for (int q = 0; q < 4; ++q) sum[q] = *reinterpret_cast<const float4*>(src + q * 256);
+  for (int k0 = 1; k0 < ks; k0 += 4) {  // up to four parts' loads in flight, added in order
+    float4 v[4][4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (k0 + u < ks) v[u][q] = *reinterpret_cast<const float4*>(src + (k0 + u) * pstride + q * 256);
+      for (int q = 0; q < 4; ++q)
+        if (k0 + u < ks) v[u][q] = *reinterpret_cast<const float4*>(src + (k0 + u) * pstride + q * 256);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (k0 + u < ks) {
-            sum[q].x += v[u][q].x;
-            sum[q].y += v[u][q].y;
-            sum[q].z += v[u][q].z;
-            sum[q].w += v[u][q].w;
-          }
+      for (int q = 0; q < 4; ++q)
+        if (k0 + u < ks) {
+          sum[q].x += v[u][q].x;
+          sum[q].y += v[u][q].y;
+          sum[q].z += v[u][q].z;
+          sum[q].w += v[u][q].w;
+        }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = 32 * w + 8 * q + 4 * hh;
+    float v[4] = {sum[q].x, sum[q].y, sum[q].z, sum[q].w};
+    if (BIAS) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] += E::to_f(a.bias[rt * BN + row + i]);
     }
-    const int tok = tb * 32 + r32;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int row = 32 * w + 8 * q + 4 * hh;
-      float v[4] = {sum[q].x, sum[q].y, sum[q].z, sum[q].w};
-      if (BIAS) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] += E::to_f(a.bias[rt * BN + row + i]);
-      }
-      uint2 packed;
-      packed.x = E::from_f(v[0]) | (E::from_f(v[1]) << 16);
-      packed.y = E::from_f(v[2]) | (E::from_f(v[3]) << 16);
-      *reinterpret_cast<uint2*>(sO + tok * LDO + row) = packed;
-    }
+    uint2 packed;
+    packed.x = E::from_f(v[0]) | (E::from_f(v[1]) << 16);
+    packed.y = E::from_f(v[2]) | (E::from_f(v[3]) << 16);
+    *reinterpret_cast<uint2*>(sO + r32 * LDO + row) = packed;
   }
   __syncthreads();
-  scatter_tile<E, D, BT, COMMIT, LDO, NT>(a, sO, rt * BN, sp * BT, tid, COMMIT ? smap : nullptr);
+  scatter_tile<E, D, 32, COMMIT, LDO, NT>(a, sO, rt * BN, sp * BT + tb * 32, tid,
+                                          COMMIT ? smap : nullptr);
 }
 
 template <bool FP16, int D, bool BIAS, bool COMMIT, int BT>
@@ -920,12 +932,13 @@ hipError_t launch_stream_nb(const WriteArgs& a, int64_t row_tiles, int splits, i
     WriteArgs b = a;
     b.ksplits = ks;
     hipLaunchKernelGGL((ctx_kv_stream_kernel<FP16, D, BIAS, COMMIT, NB>),
-                       dim3((uint32_t)(row_tiles * splits * ks)), dim3(512), 0, stream, b, splits);
+                       dim3((uint32_t)((row_tiles * ks + 7) / 8 * 8 * splits)), dim3(512), 0, stream,
+                       b, splits);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if constexpr (D != kRowsOut)
       hipLaunchKernelGGL((ctx_kv_stream_reduce<FP16, D, BIAS, COMMIT, NB>),
-                         dim3((uint32_t)(row_tiles * splits)), dim3(512), 0, stream, b, splits);
+                         dim3((uint32_t)(row_tiles * splits * NB)), dim3(256), 0, stream, b, splits);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((ctx_kv_stream_kernel<FP16, D, BIAS, COMMIT, NB>),
