@@ -958,13 +958,18 @@ hipError_t launch_by_rows(const WriteArgs& a, int num_cus, hipStream_t stream) {
   int64_t nb = (blocks + splits - 1) / splits;
   splits = (blocks + nb - 1) / nb;
   // With K split over workgroups as well, fewer token splits (each weight
-  // line requested by fewer workgroups) and more K parts cost less: at most
-  // kKSplitTokenSplits splits of up to 4 blocks.
-  if (D != kRowsOut && splits > kKSplitTokenSplits &&
-      write_ksplits(a, row_tiles, splits, (int)nb, num_cus) > 1) {
-    const int64_t s2 = (blocks + 3) / 4 > kKSplitTokenSplits ? (blocks + 3) / 4 : kKSplitTokenSplits;
-    nb = (blocks + s2 - 1) / s2;
-    splits = (blocks + nb - 1) / nb;
+  // line requested by fewer workgroups) and more K parts cost less: the
+  // K-split plan takes at most kKSplitTokenSplits splits of up to 4 blocks,
+  // and is used where that plan leaves at least half of the device idle.
+  if (D != kRowsOut) {
+    int64_t s2 = splits < kKSplitTokenSplits ? splits : kKSplitTokenSplits;
+    if ((blocks + 3) / 4 > s2) s2 = (blocks + 3) / 4;
+    const int64_t nb2 = (blocks + s2 - 1) / s2;
+    s2 = (blocks + nb2 - 1) / nb2;
+    if (write_ksplits(a, row_tiles, s2, (int)nb2, num_cus) > 1) {
+      splits = s2;
+      nb = nb2;
+    }
   }
   switch (nb) {
     case 1: return launch_stream_nb<FP16, D, BIAS, COMMIT, 1>(a, row_tiles, (int)splits, num_cus, stream);

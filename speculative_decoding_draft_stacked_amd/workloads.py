@@ -192,13 +192,16 @@ WORKLOADS = {
     # Wide hidden, head_dim 64: 64 requests x 8 columns with commit_lens.
     "wide_gqa_d64": dict(T=512, H=7168, L=5, NH=8, D=64, dtype=BF16, row_width=8, theta=5e4,
                          P=32768, slots=131072),
-    # One GPU's share of decode_commit when the KV heads are split over 8 GPUs
-    # (each GPU packs and writes one KV head of every layer; nothing is exchanged).
+    # One GPU's share of decode_commit when the KV heads are split over 8 (or 4)
+    # GPUs: each GPU packs and writes 1 (or 2) KV heads of every layer; nothing
+    # is exchanged.
     "decode_commit_kv1": dict(T=256, H=4096, L=5, NH=1, D=128, dtype=BF16, row_width=8,
+                              theta=1e6, P=32768, slots=65536),
+    "decode_commit_kv2": dict(T=256, H=4096, L=5, NH=2, D=128, dtype=BF16, row_width=8,
                               theta=1e6, P=32768, slots=65536),
 }
 WORKLOAD_ORDER = ["tiny", "decode_commit", "prefill_8k", "biased_fp16", "wide_gqa_d64",
-                  "decode_commit_kv1"]
+                  "decode_commit_kv1", "decode_commit_kv2"]
 
 
 def workload(name: str) -> Case:

@@ -103,11 +103,11 @@ def test_k_norm_weight_fp32_and_padded_pool_rows():
 K_SPLIT = {
     # few weight tiles for the device: K is split over workgroups as well, the
     # parts are added in order by a second launch before the epilogue
-    "no_commit_7_splits_4_parts": dict(T=200, H=2048, L=2, NH=1, D=128, slots=512),
+    "no_commit_4_splits_4_parts": dict(T=200, H=2048, L=2, NH=1, D=128, slots=512),
     "fp16_d64_bias_commit_2_parts": dict(T=96, H=1024, L=1, NH=2, D=64, dtype="fp16", bias=True,
                                          row_width=6, commit_range=(0, 7), neg_loc_frac=0.1,
                                          slots=256),
-    "window_1024_32_splits": dict(T=1024, H=4096, L=1, NH=1, D=128, row_width=8, slots=2048),
+    "window_1024_8_splits_8_parts": dict(T=1024, H=4096, L=1, NH=1, D=128, row_width=8, slots=2048),
 }
 
 
@@ -145,7 +145,7 @@ def _sample_rows(case, n, seed):
 
 @pytest.mark.parametrize("name,sample", [
     ("tiny", None), ("decode_commit", None), ("wide_gqa_d64", None), ("biased_fp16", 768),
-    ("prefill_8k", 384), ("decode_commit_kv1", None)])
+    ("prefill_8k", 384), ("decode_commit_kv1", None), ("decode_commit_kv2", None)])
 def test_workload(name, sample):
     case = W.workload(name)
     rows = None if sample is None else _sample_rows(case, sample, 5)

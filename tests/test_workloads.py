@@ -37,7 +37,8 @@ def test_tiny_workload_shape_and_statistics():
     assert not np.array_equal(c.qkv_w[0], c.qkv_w[1])       # distinct per layer
 
 
-@pytest.mark.parametrize("name", ["decode_commit", "wide_gqa_d64", "decode_commit_kv1"])
+@pytest.mark.parametrize("name", ["decode_commit", "wide_gqa_d64", "decode_commit_kv1",
+                                  "decode_commit_kv2"])
 def test_commit_workloads_windows(name):
     spec = W.WORKLOADS[name]
     # cheap copy of the index structure without drawing the full weights
