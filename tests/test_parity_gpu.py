@@ -108,6 +108,8 @@ K_SPLIT = {
                                          row_width=6, commit_range=(0, 7), neg_loc_frac=0.1,
                                          slots=256),
     "window_1024_8_splits_8_parts": dict(T=1024, H=4096, L=1, NH=1, D=128, row_width=8, slots=2048),
+    "fp16_d128_bias_4_splits_2_parts": dict(T=128, H=1024, L=1, NH=1, D=128, dtype="fp16",
+                                            bias=True, slots=300),
 }
 
 
