@@ -292,8 +292,11 @@ def test_all_rows_skipped_and_empty():
     assert pack.range_errors() == 0
 
 
-def test_out_of_range_rows_are_skipped_and_counted():
-    case = W.make_case(T=20, H=64, L=2, NH=1, D=64, slots=32, P=64, seed=28)
+@pytest.mark.parametrize("H", [64, 1024], ids=["plain", "k_split"])
+def test_out_of_range_rows_are_skipped_and_counted(H):
+    # H = 1024: two weight tiles and 16 chunks of 64, so K is split over
+    # workgroups and the count comes from the reduce launch
+    case = W.make_case(T=20, H=H, L=2, NH=1, D=64, slots=32, P=64, seed=28)
     case.positions[3] = 64       # == P
     case.positions[5] = -2
     case.locs[7] = 32            # == slots
