@@ -361,10 +361,13 @@ def test_rope_tables_by_content():
     assert dk.FALLBACK_REASONS[dk.last_fallback_reason] == "ROPE"
 
 
-def test_graph_replays_match_eager():
+@pytest.mark.parametrize("H", [192, 1024], ids=["plain", "k_split"])
+def test_graph_replays_match_eager(H):
     """The write captured in a HIP graph (as the benchmark times it) gives the
-    eager result on every replay, with eager work and syncs between replays."""
-    case = W.make_case(T=96, H=192, L=2, NH=2, D=128, row_width=8, slots=256, seed=31)
+    eager result on every replay, with eager work and syncs between replays.
+    At H = 1024 K is split over workgroups: two launches per write, sharing
+    the pack's workspace across replays."""
+    case = W.make_case(T=96, H=H, L=2, NH=2, D=128, row_width=8, slots=256, seed=31)
     dc, pack, _ = _run(case, "eager reference")
     k_ref, v_ref = dc.pools_host()
     side = torch.cuda.Stream()
