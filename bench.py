@@ -175,6 +175,38 @@ def copy_probe() -> None:
     print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "copies": 3}))
 
 
+def blas_probe(args) -> int:
+    """Second denominator: hipBLASLt (torch.matmul) on the bare GEMM of a write
+    workload, Y [T, N] = X [T, H] @ W^T, timed like the write (HIP graph,
+    events on the launch stream) with as many rotating weight copies, so that
+    each step reads its weight from HBM. No norm, rotation or scatter."""
+    import torch
+
+    from speculative_decoding_draft_stacked_amd import workloads as W
+
+    spec = W.WORKLOADS[args.workload]
+    T, H = spec["T"], spec["H"]
+    N = spec["L"] * 2 * spec["NH"] * spec["D"]
+    dt = torch.float16 if spec.get("dtype") == W.FP16 else torch.bfloat16
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    x = torch.randn(T, H, device="cuda", dtype=dt, generator=gen)
+    copies = max(1, math.ceil(2 * INFINITY_CACHE_BYTES / (N * H * 2)))
+    # each weight stored [H, N] contiguous: a plain (non-batched) product with
+    # no transposed operand
+    wts = [torch.randn(H, N, device="cuda", dtype=dt, generator=gen) for _ in range(copies)]
+    out = torch.empty(T, N, device="cuda", dtype=dt)
+
+    def step(i):
+        torch.matmul(x, wts[i % copies], out=out)
+
+    gpu_ms, _, launch = time_steps(step, args.steps, args.warmup, args.eager)
+    t = gpu_ms * 1e-3 / args.steps
+    print(json.dumps({"blas_probe": args.workload, "gemm": [T, N, H], "dtype": str(dt),
+                      "weight_copies": copies, "launch": launch, "us": round(t * 1e6, 2),
+                      "tflops": round(2.0 * T * N * H / t / 1e12, 1)}))
+    return 0
+
+
 def cpu_baseline(case, seconds: float) -> dict:
     """The CPU oracle on the same batch, repeated for about `seconds`."""
     import numpy as np
@@ -551,6 +583,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch steps one by one (no graph)")
+    ap.add_argument("--blas-probe", action="store_true",
+                    help="time hipBLASLt (torch.matmul) on the bare GEMM of --workload")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
     ap.add_argument("--record-traffic", nargs=5,
@@ -584,6 +618,8 @@ def main() -> int:
         return 1
     dk.lib()
     torch.cuda.set_device(0)
+    if args.blas_probe:
+        return blas_probe(args)
     if is_qk(args.workload):
         return run_qk(args)
     if is_verify(args.workload):
