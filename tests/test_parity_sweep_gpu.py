@@ -6,8 +6,10 @@ against the CPU oracle, to the same bar as the named cases: the written
 Each case draws T, H, L, KV heads, head_dim, dtype, bias, and the slot map
 (plain slots with holes, or commit windows with lengths 0..W+2) from one
 seed, so the sweep crosses both kernels, their tile and token-split choices,
-K tails, commit-window compaction and its limit. Sizes keep the fp64 oracle
-to about a second per case.
+K tails, commit-window compaction and its limit. A second sweep draws shapes
+with few weight tiles, H >= 1024 and T <= 1024, which take the K-split form
+(K parts over workgroups, parts added in a second launch). Sizes keep the
+fp64 oracle to about a second per case.
 """
 
 import numpy as np
@@ -75,3 +77,51 @@ def test_random_shape(i):
     assert pack.range_errors() == 0
     say(f"  ok: {st}")
     pack.free()
+
+
+# ------------------------------------------------ shapes for the K-split form
+
+N_KSPLIT_CASES = 24
+
+
+def _draw_ksplit(i):
+    """Few 128-row weight tiles (1 to 6), H >= 1024 and T <= 1024: most such
+    shapes split K over workgroups and add the parts in a second launch."""
+    rng = np.random.default_rng(9500 + i)
+    D = int(rng.choice([64, 128]))
+    NH = int(rng.integers(1, 3))
+    L = int(rng.integers(1, 4))
+    H = int(rng.integers(128, 513)) * 8
+    n_tot = L * 2 * NH * D
+    dtype = "fp16" if rng.random() < 0.3 else "bf16"
+    bias = bool(rng.random() < 0.3)
+    T = int(rng.integers(1, 1025))
+    while T > 1 and T * n_tot * H > 4e9:
+        T = T * 2 // 3
+    kw = dict(name=f"ksweep{i}", T=T, H=H, L=L, NH=NH, D=D, dtype=dtype, bias=bias,
+              seed=9500 + i, theta=float(rng.choice([1e4, 5e4, 1e6])), P=4096)
+    if rng.random() < 0.6:
+        Wd = int(rng.integers(1, 17))
+        T = max(Wd, T // Wd * Wd)
+        kw.update(T=T, row_width=Wd, commit_range=(0, Wd + 2))
+    kw["neg_loc_frac"] = float(rng.choice([0.0, 0.0, 0.1]))
+    kw["slots"] = T + int(rng.integers(0, 64))
+    return kw
+
+
+@pytest.mark.parametrize("i", range(N_KSPLIT_CASES))
+def test_random_shape_k_split(i):
+    kw = _draw_ksplit(i)
+    case = W.make_case(**kw)
+    say(f"[ksweep {i}] T={case.T} H={case.H} L={case.L} NH={case.NH} D={case.D} {case.dtype} "
+        f"bias={case.qkv_b is not None} W={case.row_width}")
+    dc = DeviceCase(case)
+    pack = dc.pack()
+    assert dc.write(pack)
+    torch.cuda.synchronize()
+    check_slot_sets(dc)
+    st = compare_rows(dc, None, f"ksweep{i}")
+    assert pack.range_errors() == 0
+    say(f"  ok: {st}")
+    pack.free()
+
