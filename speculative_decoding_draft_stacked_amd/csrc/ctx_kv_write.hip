@@ -15,9 +15,13 @@
 // head of 128 or two heads of 64, so a tile never straddles a head and the
 // norm and the (d, d + D/2) rotation pairs are local to it. The weight comes
 // from the pack in a blocked layout where each wave's MFMA A fragment for one
-// 16-wide K step is one contiguous KiB. Two kernels cover the two regimes:
+// 16-wide K step is one contiguous KiB. The regimes:
 //   - ctx_kv_stream_kernel, small T: one 128-row tile x up to 128 tokens per
 //     workgroup, the weight streamed from HBM into registers;
+//   - the same kernel with K split over workgroups, when few weight tiles
+//     would leave the device idle (e.g. one GPU's share of the KV heads): fp32
+//     part sums to the pack's workspace, then ctx_kv_stream_reduce adds them
+//     in part order and runs the epilogue;
 //   - ctx_kv_tiled_kernel, large T: 256 rows x 128/192/256 tokens per
 //     workgroup, both operands staged through an LDS ring by direct-to-LDS
 //     loads.
