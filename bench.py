@@ -3,7 +3,16 @@
 
 One step = one dspark_ctx_kv_write over one batch of the workload (GEMM + K
 RMSNorm + neox RoPE + scatter into every layer's pool), inputs resident in HBM.
-Prints ONE JSON line on stdout; progress goes to stderr. The workloads
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+Default run (no --workload): the headline is prefill_8k (8192 rows, the
+largest configuration that fits one GPU): `value`, `roofline` and
+`cpu_baseline` are its own. Every write configuration (tiny, decode_commit,
+prefill_8k, biased_fp16, wide_gqa_d64 and one GPU's KV-head share of
+decode_commit at 1 and 2 heads) is then timed the same way and reported under
+`configs`, each with its roofline against the work its kernels execute, the
+spread over repeated replays, and hipBLASLt's time for the bare GEMM of the
+same shape (a measured second denominator). The workloads
 qk_decode and qk_prefill_8k time the in-place table QK-RMSNorm + neox RoPE
 (dspark_table_qk_norm_rope) instead, one call per step, and verify_decode and
 verify_wide time the accept length + bonus token (dspark_verify_accept), and
@@ -33,6 +42,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "context-KV rows/s (fused GEMM+norm+RoPE+write); % of MFMA/HBM roofline"
+HEADLINE = "prefill_8k"
+WRITE_CONFIGS = ["tiny", "decode_commit", "prefill_8k", "biased_fp16", "wide_gqa_d64",
+                 "decode_commit_kv1", "decode_commit_kv2"]
+SPREAD_REPLAYS = 15  # extra graph replays after the timed one, for median / p10 / p90
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
 INFINITY_CACHE_BYTES = 256 << 20
@@ -68,6 +81,16 @@ def algorithmic(case, written_rows: int) -> dict:
               + case.L * case.D * 4 + case.T * case.D * 4 + 16 * case.T
               + 8 * case.num_requests + written_rows * n_tot * s)
     return {"flops": flops, "bytes": float(nbytes)}
+
+
+def executed(case, written_rows: int, plan: dict) -> dict:
+    """FLOPs and bytes of the work the write's kernels execute: where the plan
+    compacts a commit window, only the stored rows are projected (the bytes
+    are the same: weight, hidden rows, table rows and index arrays are read,
+    the stored rows written)."""
+    alg = algorithmic(case, written_rows)
+    rows = written_rows if plan.get("compacts") else case.T
+    return {"flops": 2.0 * rows * case.n_tot * case.H, "bytes": alg["bytes"], "rows": rows}
 
 
 def qk_algorithmic(c) -> dict:
@@ -224,10 +247,14 @@ def cpu_baseline(case, seconds: float) -> dict:
         if el >= seconds:
             break
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    affinity = len(os.sched_getaffinity(0))
     del ks, vs, np
-    return {"value": case.T * reps / el, "unit": "rows/s", "cores": int(threads), "kind": "oracle",
+    return {"value": case.T * reps / el, "unit": "rows/s", "cores": int(min(threads, affinity)),
+            "kind": "oracle",
             "sample": f"{reps} full passes of the {case.name} batch ({case.T} rows, {case.L} "
-                      f"layers) in {el:.1f} s; numpy fp64, BLAS threads = {threads}"}
+                      f"layers) in {el:.1f} s; numpy fp64 with BLAS dgemm for the projection "
+                      f"({threads} BLAS threads on {affinity} cores in the process's affinity "
+                      f"mask), Python loops for the scatter"}
 
 
 def qk_cpu_baseline(c, seconds: float) -> dict:
@@ -252,9 +279,11 @@ def qk_cpu_baseline(c, seconds: float) -> dict:
                       f"{threads}"}
 
 
-def time_steps(step, steps: int, warmup: int, eager: bool):
+def time_steps(step, steps: int, warmup: int, eager: bool, spread: list = None):
     """Warm up, then time exactly `steps` calls of step(i) with events on the
-    stream they run on. Returns (device ms, wall s, launch mode)."""
+    stream they run on. Returns (device ms, wall s, launch mode). With a list
+    in `spread`, the captured graph is then replayed SPREAD_REPLAYS more times
+    and each replay's device ms per step is appended to it."""
     import torch
 
     for i in range(warmup):
@@ -288,7 +317,69 @@ def time_steps(step, steps: int, warmup: int, eager: bool):
     g_main.replay()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1), time.perf_counter() - t0, "hip_graph"
+    total, wall = e0.elapsed_time(e1), time.perf_counter() - t0
+    if spread is not None:
+        spread.append(total / steps)
+        for _ in range(SPREAD_REPLAYS):
+            e0.record()
+            g_main.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            spread.append(e0.elapsed_time(e1) / steps)
+    return total, wall, "hip_graph"
+
+
+def percentiles(xs: list) -> dict:
+    """Median, p10 and p90 of per-step times (ms) -> microseconds."""
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64) * 1e3
+    return {"us_median": round(float(np.median(a)), 2),
+            "us_p10": round(float(np.percentile(a, 10)), 2),
+            "us_p90": round(float(np.percentile(a, 90)), 2), "replays": len(xs)}
+
+
+def blas_time_us(T: int, N: int, H: int, fp16: bool, steps: int, warmup: int) -> float:
+    """hipBLASLt (torch.matmul) on the bare GEMM Y [T, N] = X [T, H] @ W^T, timed
+    like the write (HIP graph, events on the launch stream) with rotating
+    weight copies that exceed the Infinity Cache, so each step reads its
+    weight from HBM. No norm, rotation or scatter."""
+    import torch
+
+    dt = torch.float16 if fp16 else torch.bfloat16
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    x = torch.randn(T, H, device="cuda", dtype=dt, generator=gen)
+    copies = max(1, math.ceil(2 * INFINITY_CACHE_BYTES / (N * H * 2)))
+    wts = [torch.randn(H, N, device="cuda", dtype=dt, generator=gen) for _ in range(copies)]
+    out = torch.empty(T, N, device="cuda", dtype=dt)
+
+    def step(i):
+        torch.matmul(x, wts[i % copies], out=out)
+
+    ms, _, _ = time_steps(step, steps, warmup, False)
+    del x, wts, out
+    torch.cuda.empty_cache()
+    return ms * 1e3 / steps
+
+
+def hbm_ceilings(steps: int = 20) -> dict:
+    """Measured HBM rates of plain torch kernels on 1 GiB buffers: a device copy
+    (read + write) and a sum reduction (read only); a second denominator for
+    the HBM-bound rows."""
+    import torch
+
+    n = COPY_PROBE_BYTES // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    acc = torch.empty((), dtype=torch.float32, device="cuda")
+    out = {}
+    for name, fn, nbytes in (("copy", lambda i: dst.copy_(src), 2 * COPY_PROBE_BYTES),
+                             ("read_sum", lambda i: torch.sum(src, dtype=torch.float32, out=acc),
+                              COPY_PROBE_BYTES)):
+        ms, _, _ = time_steps(fn, steps, 3, True)
+        out[name + "_gbs"] = round(nbytes * steps / (ms * 1e-3) / 1e9, 1)
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
 
 
 def roofline(alg: dict, t_kernel: float, workload: str) -> dict:
@@ -577,9 +668,11 @@ def run_attn(args) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode_commit")
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="all",
+                    help="all (default: prefill_8k headline + every write configuration) or "
+                         "one workload")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch steps one by one (no graph)")
@@ -606,12 +699,9 @@ def main() -> int:
               file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     import speculative_decoding_draft_stacked_amd as dk
-    from speculative_decoding_draft_stacked_amd import workloads as W
-    from speculative_decoding_draft_stacked_amd.harness import DeviceCase
 
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
@@ -629,8 +719,25 @@ def main() -> int:
     if is_attn(args.workload):
         return run_attn(args)
 
-    log(f"[bench] generating workload {args.workload}")
-    case = W.workload(args.workload)
+    if args.workload == "all":
+        return run_all(args)
+    rec = run_write(args.workload, args, cpu=not args.no_cpu_baseline)
+    print(json.dumps(headline_line(rec, args)), flush=True)
+    return 0
+
+
+def run_write(name: str, args, cpu: bool = False, blas: bool = False) -> dict:
+    """Time the write on one workload; returns its record (see headline_line
+    and run_all for how it is reported)."""
+    import numpy as np
+    import torch
+
+    import speculative_decoding_draft_stacked_amd as dk
+    from speculative_decoding_draft_stacked_amd import workloads as W
+    from speculative_decoding_draft_stacked_amd.harness import DeviceCase
+
+    log(f"[bench] generating workload {name}")
+    case = W.workload(name)
     valid = (case.locs >= 0)
     if case.commit_lens is not None:
         t = np.arange(case.T)
@@ -645,24 +752,70 @@ def main() -> int:
     pools = dc.pool_descs()
     commit = dc.commit
     W_ = case.row_width if commit is not None else None
-    log(f"[bench] T={case.T} H={case.H} L={case.L} NH={case.NH} D={case.D} {case.dtype}, "
-        f"written rows {written}, weight copies {copies}")
+    plan = packs[0].plan(case.T, commit is not None)
+    ws = dc.workspace(packs[0])
+    exe = executed(case, written, plan)
+    log(f"[bench] {name}: T={case.T} H={case.H} L={case.L} NH={case.NH} D={case.D} "
+        f"{case.dtype}, written rows {written}, weight copies {copies}, plan {plan}")
 
     def step(i):
         ok = dk.ctx_kv_write(packs[i % copies], dc.x, dc.positions, dc.locs, pools,
-                             commit_lens=commit, locs_row_width=W_)
+                             commit_lens=commit, locs_row_width=W_, workspace=ws,
+                             range_errors=dc.err)
         if not ok:
             raise RuntimeError("write fell back")
 
-    # warmup (eager) also validates the launch path before capture
-    gpu_ms, wall, launch = time_steps(step, args.steps, args.warmup, args.eager)
-    assert packs[0].range_errors() == 0
-    log(f"[bench] {args.steps} steps: device {gpu_ms:.3f} ms, wall {wall * 1e3:.3f} ms")
-
+    spread = []
+    gpu_ms, wall, launch = time_steps(step, args.steps, args.warmup, args.eager, spread)
+    assert dc.range_errors() == 0
+    log(f"[bench] {name}: {args.steps} steps: device {gpu_ms:.3f} ms, wall {wall * 1e3:.3f} ms")
     ms_per_step = gpu_ms / args.steps
-    t_kernel = ms_per_step * 1e-3  # one kernel per step
-    roof = roofline(alg, t_kernel, args.workload)
+    t_kernel = ms_per_step * 1e-3
+    rec = {
+        "workload": name, "case": case, "written": written, "alg": alg, "exe": exe, "plan": plan,
+        "copies": copies, "launch": launch, "gpu_ms": gpu_ms, "ms_per_step": ms_per_step,
+        "spread": percentiles(spread) if spread else None,
+        "roofline": roofline(exe, t_kernel, name),
+    }
+    for p in packs:
+        p.free()
+    del packs, dc, ws
+    torch.cuda.empty_cache()
+    if blas:
+        rec["hipblaslt_us"] = round(blas_time_us(case.T, case.n_tot, case.H, case.dtype == "fp16",
+                                                 args.steps, args.warmup), 2)
+    if cpu:
+        log(f"[bench] timing the CPU oracle for ~{args.cpu_seconds} s")
+        rec["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    return rec
 
+
+def config_entry(rec: dict) -> dict:
+    """One workload's entry of the `configs` record."""
+    case = rec["case"]
+    t = rec["ms_per_step"] * 1e-3
+    e = {
+        "T": case.T, "H": case.H, "L": case.L, "kv_heads": case.NH, "head_dim": case.D,
+        "dtype": case.dtype, "bias": case.qkv_b is not None,
+        "commit_window": case.row_width or None, "written_rows": rec["written"],
+        "plan": rec["plan"], "us_per_step": round(rec["ms_per_step"] * 1e3, 2),
+        "rows_per_s": round(case.T / t, 1), "written_rows_per_s": round(rec["written"] / t, 1),
+        "projected_rows": rec["exe"]["rows"],
+        "method_flops": rec["alg"]["flops"], "executed_flops": rec["exe"]["flops"],
+        "algorithmic_bytes": rec["alg"]["bytes"], "roofline": rec["roofline"],
+    }
+    if rec.get("spread"):
+        e.update(rec["spread"])
+    if "hipblaslt_us" in rec:
+        e["hipblaslt_bare_gemm_us"] = rec["hipblaslt_us"]
+        e["vs_hipblaslt_bare_gemm"] = round(rec["hipblaslt_us"] / (rec["ms_per_step"] * 1e3), 3)
+    return e
+
+
+def headline_line(rec: dict, args) -> dict:
+    """The contract's JSON line for one write workload."""
+    case = rec["case"]
+    t_kernel = rec["ms_per_step"] * 1e-3
     out = {
         "metric": METRIC,
         "value": round(case.T / t_kernel, 1),
@@ -670,24 +823,45 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 6),
+        "ms_per_step": round(rec["ms_per_step"], 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": case.dtype,
         "data": "synthetic: seeded random inputs and random-init weights of the workload's shape",
-        "config": {"workload": args.workload, "T": case.T, "H": case.H, "L": case.L,
-                   "kv_heads": case.NH, "head_dim": case.D, "written_rows": written,
-                   "written_rows_per_s": round(written / t_kernel, 1),
-                   "weight_copies": copies, "launch": launch,
-                   "algorithmic_bytes": alg["bytes"], "flops": alg["flops"]},
-        "roofline": roof,
+        "config": {"workload": rec["workload"], "T": case.T, "H": case.H, "L": case.L,
+                   "kv_heads": case.NH, "head_dim": case.D, "written_rows": rec["written"],
+                   "written_rows_per_s": round(rec["written"] / t_kernel, 1),
+                   "weight_copies": rec["copies"], "launch": rec["launch"], "plan": rec["plan"],
+                   "algorithmic_bytes": rec["alg"]["bytes"], "flops": rec["alg"]["flops"],
+                   "executed_flops": rec["exe"]["flops"]},
+        "roofline": rec["roofline"],
     }
-    if not args.no_cpu_baseline:
-        log(f"[bench] timing the CPU oracle for ~{args.cpu_seconds} s")
-        out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
-    for p in packs:
-        p.free()
+    if rec.get("spread"):
+        out["config"].update(rec["spread"])
+    if "cpu_baseline" in rec:
+        out["cpu_baseline"] = rec["cpu_baseline"]
+    return out
+
+
+def run_all(args) -> int:
+    """The headline (prefill_8k: value, roofline, cpu_baseline) plus every
+    write configuration under `configs`, and the measured HBM ceilings."""
+    head = run_write(HEADLINE, args, cpu=not args.no_cpu_baseline, blas=True)
+    out = headline_line(head, args)
+    configs = {}
+    for name in WRITE_CONFIGS:
+        rec = head if name == HEADLINE else run_write(name, args, blas=True)
+        configs[name] = config_entry(rec)
+    out["configs"] = configs
+    ceil = hbm_ceilings()
+    out["measured_peak"] = {
+        **ceil,
+        "hipblaslt_bare_gemm_us": head.get("hipblaslt_us"),
+        "note": "second denominators measured in this run: hipBLASLt (torch.matmul) on each "
+                "workload's bare GEMM with rotating weights (configs.*.hipblaslt_bare_gemm_us), "
+                "and torch's 1 GiB copy and sum kernels for HBM",
+    }
     print(json.dumps(out), flush=True)
     return 0
 

@@ -22,8 +22,10 @@
  *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.
  *   - Status codes are the DSPARK_* values below. A call that returns anything
  *     but DSPARK_OK has enqueued no device work.
- *   - The library never synchronises the stream in dspark_ctx_kv_write and
- *     allocates nothing there, so the call can be captured in a HIP graph.
+ *   - The calls that enqueue work (the write, the QK op, the verify step, the
+ *     producer, the attention) allocate nothing and never synchronise the
+ *     stream, so they can be captured in a HIP graph (the write's validate mode
+ *     excepted); the pack calls allocate and synchronise.
  */
 #ifndef DSPARK_H
 #define DSPARK_H
@@ -39,6 +41,8 @@ enum {
   DSPARK_OK = 0,
   DSPARK_FALLBACK = 1,     /* not eligible: the caller runs its per-layer path */
   DSPARK_E_INVALID = -1,   /* misuse: bad pointer, size or argument pairing */
+  DSPARK_E_RANGE = -2,     /* validate mode: a stored row's position or slot is out of range,
+                              or two stored rows name one slot (see DSPARK_RANGE_*) */
   DSPARK_E_DEVICE = -3,    /* a HIP runtime call failed */
   DSPARK_E_NOMEM = -4      /* device allocation failed (pack only) */
 };
@@ -56,6 +60,31 @@ enum {
   DSPARK_FB_KV_SCALE = 8,        /* a K/V quantization scale is attached */
   DSPARK_FB_ROPE = 9,            /* rotary is not neox full-dim over one shared fp32 table */
   DSPARK_FB_POOL_LAYOUT = 10     /* pool dtype, head layout or alignment unsupported */
+};
+
+/* What a DSPARK_E_RANGE return of the write's validate mode found. */
+enum {
+  DSPARK_RANGE_NONE = 0,
+  DSPARK_RANGE_POSITION = 1,   /* a stored row's position is outside [0, rope_max_pos) */
+  DSPARK_RANGE_SLOT = 2,       /* a stored row's loc is >= a layer's num_slots */
+  DSPARK_RANGE_DUPLICATE = 3   /* two stored rows name the same slot */
+};
+
+/* Flags of dspark_ctx_kv_write. */
+enum {
+  /* Before enqueueing, copy positions, locs and commit_lens to the host
+   * (synchronising `stream`) and check the rows that would be stored; any
+   * DSPARK_RANGE_* finding returns DSPARK_E_RANGE with nothing enqueued. Not
+   * usable under stream capture. Without it the write trusts these
+   * preconditions and only guards memory (see dspark_ctx_kv_write). */
+  DSPARK_WRITE_VALIDATE = 1
+};
+
+/* Kernels a write can run (dspark_ctx_kv_plan). */
+enum {
+  DSPARK_KERNEL_STREAM = 0,         /* weight-streaming kernel, one launch */
+  DSPARK_KERNEL_STREAM_KSPLIT = 1,  /* streaming kernel over K parts + a reduce launch */
+  DSPARK_KERNEL_TILED = 2           /* LDS-tiled MFMA kernel, one launch */
 };
 
 /* Element types. */
@@ -130,17 +159,44 @@ int dspark_check_eligibility(const dspark_layer_desc* layers, int32_t num_layers
  * tables whose pointers differ, then allocates and fills on `stream`:
  * W_stacked [L*2*kv, hidden] (layer-major, K rows then V rows), the stacked bias
  * [L*2*kv] when present, k_norm [L, head_dim] widened to fp32. The rotary table
- * of layer 0 is referenced, not copied: it must outlive the pack. When the
- * weight has at most (compute units / 2) 128-row tiles, the pack also
- * allocates a workspace for the write's K-split form (128 x 128 fp32 per
- * compute unit, 16 MiB on 256 CUs, and a row map). Synchronises
+ * of layer 0 is referenced, not copied: it must outlive the pack. Synchronises
  * `stream` before returning, so the source weights may change afterwards; the
- * pack then still holds the old values (re-pack after a weight update).
+ * pack then still holds the old values (re-pack after a weight update). After
+ * this call the pack is never written again: any number of writes may use it
+ * at once, on any streams.
+ * With the environment variable DSPARK_LOG set to a non-empty value other than
+ * "0", every FALLBACK of this call and the first write FALLBACK of each pack
+ * print their reason on stderr.
  * Returns DSPARK_OK with *out set, DSPARK_FALLBACK with *fallback_reason set
  * (*out = NULL), DSPARK_E_INVALID (NULL out), DSPARK_E_NOMEM or DSPARK_E_DEVICE. */
 int dspark_pack_ctx_kv(const dspark_layer_desc* layers, int32_t num_layers, int64_t hidden,
                        int32_t act_dtype, void* stream, dspark_ctx_kv_pack** out,
                        int32_t* fallback_reason);
+
+/* Launch plan of a write of num_tokens rows through `pack` on the current
+ * device (host-only; what dspark_ctx_kv_write would enqueue). */
+typedef struct {
+  int32_t kernel;          /* DSPARK_KERNEL_* */
+  int32_t token_tile;      /* tokens per workgroup (tiled: 128/192/256; streaming: 32..128) */
+  int64_t workgroups;      /* of the main launch */
+  int64_t reduce_workgroups; /* of the K-part reduce launch (0: none) */
+  int32_t k_parts;         /* K split over workgroups (1: none) */
+  int32_t compacts;        /* 1: only the rows that are stored are projected */
+  int64_t workspace_bytes; /* device workspace the write needs (0: none) */
+} dspark_write_plan;
+
+/* Fills *plan for a write of num_tokens rows (has_commit: commit_lens given).
+ * Returns DSPARK_OK, DSPARK_E_INVALID (NULL arguments, num_tokens < 0) or
+ * DSPARK_E_DEVICE. */
+int dspark_ctx_kv_plan(const dspark_ctx_kv_pack* pack, int64_t num_tokens, int32_t has_commit,
+                       dspark_write_plan* plan);
+
+/* Device workspace bytes dspark_ctx_kv_write needs for num_tokens rows
+ * (has_commit: commit_lens given): fp32 sums of K parts when the write splits
+ * K over workgroups (few weight tiles for the device, at most 128 x 128 floats
+ * per compute unit plus an 8 KiB row map), else 0. Host-only. */
+int dspark_ctx_kv_workspace_bytes(const dspark_ctx_kv_pack* pack, int64_t num_tokens,
+                                  int32_t has_commit, int64_t* bytes);
 
 /* The write: one GEMM of ctx_hidden against W_stacked, then per layer and K head
  * RMSNorm + neox rotation, and the scatter of K and raw V into the pools.
@@ -156,23 +212,31 @@ int dspark_pack_ctx_kv(const dspark_layer_desc* layers, int32_t num_layers, int6
  *     num_requests * locs_row_width == num_tokens (else DSPARK_E_INVALID).
  *     Without commit_lens, locs_row_width and num_requests must be 0.
  *   pools: host array of num_pools == L descriptors, layer order of the pack.
- * Valid slots must be distinct (the scatter is not ordered between rows).
- * Writes through one pack may use its workspace: calls that overlap in time
- * (on different streams) must use different packs.
- * A row whose position is outside [0, rope_max_pos) or whose loc is
- * >= that layer's num_slots is not written and is counted in the pack's range
- * error counter (dspark_pack_range_errors); no memory outside the given
- * buffers is ever accessed.
- * num_tokens == 0 returns DSPARK_OK with nothing enqueued.
- * Returns DSPARK_OK (enqueued on `stream`), DSPARK_FALLBACK with
- * *fallback_reason (may be NULL) = DSPARK_FB_POOL_LAYOUT, DSPARK_E_INVALID,
- * or DSPARK_E_DEVICE. */
+ *   workspace: device, 16-byte aligned, at least dspark_ctx_kv_workspace_bytes
+ *     bytes (may be NULL when that is 0). Scratch, owned by the caller: no
+ *     need to clear it; writes that overlap in time must use different
+ *     workspaces.
+ *   range_errors: device counter or NULL. A stored row whose position is
+ *     outside [0, rope_max_pos) or whose loc is >= that layer's num_slots is
+ *     not written and adds 1 per (row, layer) here (atomically, never cleared);
+ *     no memory outside the given buffers is ever accessed.
+ *   flags: 0 or DSPARK_WRITE_VALIDATE (see there).
+ * The rows that are stored must name distinct slots (the scatter is not
+ * ordered between rows); validate mode reports a violation.
+ * num_tokens == 0 returns DSPARK_OK with nothing enqueued. Without
+ * DSPARK_WRITE_VALIDATE the call never synchronises the stream and allocates
+ * nothing, so it can be captured in a HIP graph.
+ * Returns DSPARK_OK (enqueued on `stream`); DSPARK_FALLBACK with *detail (may
+ * be NULL) = DSPARK_FB_POOL_LAYOUT; DSPARK_E_RANGE (validate mode) with
+ * *detail = DSPARK_RANGE_*; DSPARK_E_INVALID; or DSPARK_E_DEVICE. */
 int dspark_ctx_kv_write(const dspark_ctx_kv_pack* pack, const void* ctx_hidden,
                         int64_t num_tokens, int64_t hidden_row_stride,
                         const int64_t* positions, const int64_t* locs,
                         const int64_t* commit_lens, int64_t locs_row_width,
                         int64_t num_requests, const dspark_pool_desc* pools,
-                        int32_t num_pools, void* stream, int32_t* fallback_reason);
+                        int32_t num_pools, void* workspace, int64_t workspace_bytes,
+                        unsigned long long* range_errors, uint32_t flags, void* stream,
+                        int32_t* detail);
 
 /* In-place table QK RMSNorm + neox RoPE on a fused QKV tensor (sglang PR
  * #31847, key source snippets: table_qk_norm_rope_ and
@@ -339,10 +403,6 @@ int dspark_draft_attention(const dspark_attn_desc* desc, int64_t num_requests, i
                            unsigned long long* range_errors, void* stream,
                            int32_t* fallback_reason);
 
-/* Reads and clears the pack's count of rows skipped for an out-of-range
- * position or slot. Synchronises `stream`. Returns DSPARK_OK or an error. */
-int dspark_pack_range_errors(const dspark_ctx_kv_pack* pack, void* stream, int64_t* count);
-
 /* Shape of a pack (host-only). Any output pointer may be NULL. */
 int dspark_pack_info(const dspark_ctx_kv_pack* pack, int32_t* num_layers, int64_t* hidden,
                      int64_t* kv_size, int64_t* head_dim, int32_t* act_dtype,
@@ -363,9 +423,10 @@ int dspark_pack_buffers(const dspark_ctx_kv_pack* pack, const void** w_stacked,
 /* Frees the pack's device buffers (waits for the device first). NULL is a no-op. */
 void dspark_pack_free(dspark_ctx_kv_pack* pack);
 
-/* Static strings for a status code and a fallback reason. */
+/* Static strings for a status code, a fallback reason and a range cause. */
 const char* dspark_status_str(int status);
 const char* dspark_fallback_str(int reason);
+const char* dspark_range_str(int cause);
 
 #ifdef __cplusplus
 }

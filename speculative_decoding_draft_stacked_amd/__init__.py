@@ -8,8 +8,13 @@ built, every call raises.
 Entry points mirror the C ABI in include/dspark.h:
   check_eligibility(layers, hidden, act_dtype)      -> (status, reason)
   pack_ctx_kv(layers, hidden, act_dtype, stream)    -> Pack | None (None = fallback)
+  Pack.plan(T, has_commit), Pack.workspace_bytes(T, has_commit)
   ctx_kv_write(pack, ctx_hidden, positions, locs, pools, commit_lens=None,
-               locs_row_width=None, stream=None)    -> True (enqueued) | False (fallback)
+               locs_row_width=None, workspace=None, range_errors=None,
+               validate=False, stream=None)         -> True (enqueued) | False (fallback)
+Misuse (wrong index dtypes, shapes, devices or layouts) raises ValueError
+before anything reaches the library; DSPARK_E_RANGE from validate mode raises
+RangeError.
 """
 
 from __future__ import annotations
@@ -21,17 +26,23 @@ from typing import Optional, Sequence
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdspark.so")
 
-OK, FALLBACK, E_INVALID, E_DEVICE, E_NOMEM = 0, 1, -1, -3, -4
+OK, FALLBACK, E_INVALID, E_RANGE, E_DEVICE, E_NOMEM = 0, 1, -1, -2, -3, -4
 BF16, FP16, FP32, QUANTIZED = 0, 1, 2, 99
+RANGE_NONE, RANGE_POSITION, RANGE_SLOT, RANGE_DUPLICATE = 0, 1, 2, 3
+WRITE_VALIDATE = 1
+KERNEL_STREAM, KERNEL_STREAM_KSPLIT, KERNEL_TILED = 0, 1, 2
+KERNEL_NAMES = {KERNEL_STREAM: "stream", KERNEL_STREAM_KSPLIT: "stream_ksplit",
+                KERNEL_TILED: "tiled"}
 MAX_LAYERS = 32
 FALLBACK_REASONS = {
     0: "NONE", 1: "NO_LAYERS", 2: "TOO_MANY_LAYERS", 3: "NOT_SLICEABLE", 4: "EPS_MISMATCH",
     5: "MIXED_BIAS", 6: "SHAPE", 7: "DTYPE", 8: "KV_SCALE", 9: "ROPE", 10: "POOL_LAYOUT",
 }
 EXPORTS = [
-    "dspark_check_eligibility", "dspark_pack_ctx_kv", "dspark_ctx_kv_write",
-    "dspark_pack_range_errors", "dspark_pack_info", "dspark_pack_buffers", "dspark_pack_free",
-    "dspark_status_str", "dspark_fallback_str", "dspark_table_qk_norm_rope",
+    "dspark_check_eligibility", "dspark_pack_ctx_kv", "dspark_ctx_kv_plan",
+    "dspark_ctx_kv_workspace_bytes", "dspark_ctx_kv_write", "dspark_pack_info",
+    "dspark_pack_buffers", "dspark_pack_free", "dspark_status_str", "dspark_fallback_str",
+    "dspark_range_str", "dspark_table_qk_norm_rope",
     "dspark_verify_accept", "dspark_pack_main_proj", "dspark_main_proj_workspace_bytes",
     "dspark_main_proj_norm", "dspark_main_proj_free", "dspark_draft_attention_workspace_bytes",
     "dspark_draft_attention",
@@ -80,6 +91,28 @@ class PoolDesc(ctypes.Structure):
     ]
 
 
+class WritePlan(ctypes.Structure):
+    """Mirror of dspark_write_plan."""
+
+    _fields_ = [
+        ("kernel", ctypes.c_int32),
+        ("token_tile", ctypes.c_int32),
+        ("workgroups", ctypes.c_int64),
+        ("reduce_workgroups", ctypes.c_int64),
+        ("k_parts", ctypes.c_int32),
+        ("compacts", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_int64),
+    ]
+
+
+class RangeError(ValueError):
+    """DSPARK_E_RANGE from the write's validate mode; ``cause`` is a RANGE_* code."""
+
+    def __init__(self, cause: int, message: str):
+        super().__init__(message)
+        self.cause = cause
+
+
 class AttnDesc(ctypes.Structure):
     """Mirror of dspark_attn_desc."""
 
@@ -121,9 +154,11 @@ def lib() -> ctypes.CDLL:
         L.dspark_check_eligibility.argtypes = [ctypes.POINTER(LayerDesc), i32, i64, i32, p_i32]
         L.dspark_pack_ctx_kv.argtypes = [ctypes.POINTER(LayerDesc), i32, i64, i32, vp,
                                          ctypes.POINTER(vp), p_i32]
+        L.dspark_ctx_kv_plan.argtypes = [vp, i64, i32, ctypes.POINTER(WritePlan)]
+        L.dspark_ctx_kv_workspace_bytes.argtypes = [vp, i64, i32, p_i64]
         L.dspark_ctx_kv_write.argtypes = [vp, vp, i64, i64, vp, vp, vp, i64, i64,
-                                          ctypes.POINTER(PoolDesc), i32, vp, p_i32]
-        L.dspark_pack_range_errors.argtypes = [vp, vp, p_i64]
+                                          ctypes.POINTER(PoolDesc), i32, vp, i64, vp,
+                                          ctypes.c_uint32, vp, p_i32]
         L.dspark_pack_info.argtypes = [vp, p_i32, p_i64, p_i64, p_i64, p_i32, p_i32]
         L.dspark_pack_buffers.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                           ctypes.POINTER(vp)]
@@ -145,8 +180,11 @@ def lib() -> ctypes.CDLL:
         L.dspark_status_str.restype = ctypes.c_char_p
         L.dspark_fallback_str.argtypes = [ctypes.c_int]
         L.dspark_fallback_str.restype = ctypes.c_char_p
+        L.dspark_range_str.argtypes = [ctypes.c_int]
+        L.dspark_range_str.restype = ctypes.c_char_p
         for name in ("dspark_check_eligibility", "dspark_pack_ctx_kv", "dspark_ctx_kv_write",
-                     "dspark_pack_range_errors", "dspark_pack_info", "dspark_pack_buffers",
+                     "dspark_ctx_kv_plan", "dspark_ctx_kv_workspace_bytes",
+                     "dspark_pack_info", "dspark_pack_buffers",
                      "dspark_table_qk_norm_rope", "dspark_verify_accept",
                      "dspark_pack_main_proj", "dspark_main_proj_workspace_bytes",
                      "dspark_main_proj_norm", "dspark_draft_attention_workspace_bytes",
@@ -162,6 +200,10 @@ def status_str(status: int) -> str:
 
 def fallback_str(reason: int) -> str:
     return lib().dspark_fallback_str(reason).decode()
+
+
+def range_str(cause: int) -> str:
+    return lib().dspark_range_str(cause).decode()
 
 
 def _raise_for(status: int, what: str):
@@ -185,10 +227,12 @@ def check_eligibility(layers: Sequence[LayerDesc], hidden: int, act_dtype: int):
 
 
 class Pack:
-    """Owner of a dspark_ctx_kv_pack handle."""
+    """Owner of a dspark_ctx_kv_pack handle. Keeps the tensors the pack
+    references (the rotary table) alive while it exists."""
 
-    def __init__(self, handle: int):
+    def __init__(self, handle: int, keep=()):
         self.handle = handle
+        self._keep = tuple(keep)
 
     @property
     def as_parameter(self):
@@ -211,16 +255,28 @@ class Pack:
                                              ctypes.byref(k)), "dspark_pack_buffers")
         return w.value, b.value, k.value
 
-    def range_errors(self, stream=None) -> int:
-        n = ctypes.c_int64()
-        _raise_for(lib().dspark_pack_range_errors(self.as_parameter, _stream(stream),
-                                                  ctypes.byref(n)), "dspark_pack_range_errors")
+    def plan(self, num_tokens: int, has_commit: bool) -> dict:
+        """dspark_ctx_kv_plan: which kernels a write of num_tokens rows runs."""
+        p = WritePlan()
+        _raise_for(lib().dspark_ctx_kv_plan(self.as_parameter, num_tokens, int(has_commit),
+                                            ctypes.byref(p)), "dspark_ctx_kv_plan")
+        return dict(kernel=KERNEL_NAMES.get(p.kernel, str(p.kernel)), token_tile=p.token_tile,
+                    workgroups=p.workgroups, reduce_workgroups=p.reduce_workgroups,
+                    k_parts=p.k_parts, compacts=bool(p.compacts),
+                    workspace_bytes=p.workspace_bytes)
+
+    def workspace_bytes(self, num_tokens: int, has_commit: bool) -> int:
+        n = ctypes.c_int64(0)
+        _raise_for(lib().dspark_ctx_kv_workspace_bytes(self.as_parameter, num_tokens,
+                                                       int(has_commit), ctypes.byref(n)),
+                   "dspark_ctx_kv_workspace_bytes")
         return n.value
 
     def free(self):
         if self.handle:
             lib().dspark_pack_free(ctypes.c_void_p(self.handle))
             self.handle = 0
+        self._keep = ()
 
     def __del__(self):
         try:
@@ -252,7 +308,8 @@ def pack_ctx_kv(layers: Sequence[LayerDesc], hidden: int, act_dtype: int, stream
     if st == FALLBACK:
         return None
     _raise_for(st, "dspark_pack_ctx_kv")
-    return Pack(h.value)
+    # the pack references layer 0's rotary table: keep its tensor alive
+    return Pack(h.value, keep=getattr(layers[0], "_tensors", ()) if len(layers) else ())
 
 
 last_fallback_reason = 0
@@ -260,14 +317,17 @@ last_fallback_reason = 0
 
 def ctx_kv_write_raw(pack: Pack, ctx_hidden: int, num_tokens: int, hidden_row_stride: int,
                      positions: int, locs: int, commit_lens: Optional[int], locs_row_width: int,
-                     num_requests: int, pools: Sequence[PoolDesc], stream) -> int:
-    """dspark_ctx_kv_write on raw device pointers; returns (status, reason)."""
+                     num_requests: int, pools: Sequence[PoolDesc], stream,
+                     workspace: Optional[int] = None, workspace_bytes: int = 0,
+                     range_errors: Optional[int] = None, flags: int = 0) -> tuple:
+    """dspark_ctx_kv_write on raw device pointers; returns (status, detail)."""
     arr = (PoolDesc * max(len(pools), 1))(*pools)
-    reason = ctypes.c_int32(0)
+    detail = ctypes.c_int32(0)
     st = lib().dspark_ctx_kv_write(pack.as_parameter, ctx_hidden, num_tokens, hidden_row_stride,
                                    positions, locs, commit_lens, locs_row_width, num_requests,
-                                   arr, len(pools), _stream(stream), ctypes.byref(reason))
-    return st, reason.value
+                                   arr, len(pools), workspace, workspace_bytes, range_errors,
+                                   flags, _stream(stream), ctypes.byref(detail))
+    return st, detail.value
 
 
 # ------------------------------------------------------------------ torch plumbing
@@ -280,8 +340,12 @@ def _dtype_code(t) -> int:
 def layer_desc(qkv_weight, k_norm_weight, eps: float, q_size: int, kv_size: int, head_dim: int,
                cos_sin_cache, qkv_bias=None, has_kv_scale: bool = False,
                is_neox: bool = True, rotary_dim: Optional[int] = None) -> LayerDesc:
-    """Descriptor of one layer from its tensors (pointers and strides only)."""
-    return LayerDesc(
+    """Descriptor of one layer from its tensors (pointers and strides only).
+    The descriptor holds a reference to the rotary table, which a pack built
+    from it keeps alive."""
+    if cos_sin_cache.dim() != 2:
+        raise ValueError("cos_sin_cache must be [max_position, rotary_dim]")
+    d = LayerDesc(
         qkv_weight=qkv_weight.data_ptr(), w_rows=qkv_weight.shape[0],
         w_row_stride=qkv_weight.stride(0), w_col_stride=qkv_weight.stride(1),
         w_dtype=_dtype_code(qkv_weight),
@@ -293,6 +357,8 @@ def layer_desc(qkv_weight, k_norm_weight, eps: float, q_size: int, kv_size: int,
         rope_dim=cos_sin_cache.shape[1] if rotary_dim is None else rotary_dim,
         rope_is_neox=int(is_neox),
     )
+    d._tensors = (cos_sin_cache,)
+    return d
 
 
 def pool_desc(k_buf, v_buf) -> PoolDesc:
@@ -305,21 +371,72 @@ def pool_desc(k_buf, v_buf) -> PoolDesc:
                     else QUANTIZED)
 
 
+_ACT_TORCH = {BF16: "bfloat16", FP16: "float16"}
+
+
+def _check_index(name: str, t, n: int, device) -> None:
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.int64:
+        raise ValueError(f"{name} must be an int64 tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.numel() != n or (n and not t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous tensor of {n} elements")
+
+
 def ctx_kv_write(pack: Pack, ctx_hidden, positions, locs, pools: Sequence[PoolDesc],
-                 commit_lens=None, locs_row_width: Optional[int] = None, stream=None) -> bool:
+                 commit_lens=None, locs_row_width: Optional[int] = None, workspace=None,
+                 range_errors=None, validate: bool = False, stream=None) -> bool:
     """Enqueue the write. True when enqueued, False on fallback (nothing
-    written). ValueError on misuse (e.g. commit_lens without locs_row_width)."""
+    written). ValueError on misuse: commit_lens without locs_row_width, index
+    tensors that are not contiguous int64 of the right length, ctx_hidden of
+    another dtype than the pack's or without unit column stride, tensors on
+    another device. ``workspace`` is a uint8 device tensor of at least
+    pack.workspace_bytes(T, commit) bytes (allocated here when None and
+    needed); ``range_errors`` an int64 device tensor of one element that counts
+    rows skipped for an out-of-range position or slot. With validate=True the
+    index arrays are checked first (the stream is synchronised) and a bad row
+    raises RangeError."""
+    import torch
     if (commit_lens is None) != (locs_row_width is None):
         raise ValueError("commit_lens and locs_row_width must be passed together")
+    info = pack.info()
+    if ctx_hidden.dim() != 2 or ctx_hidden.stride(1) != 1:
+        raise ValueError("ctx_hidden must be [T, hidden] with unit column stride")
+    if str(ctx_hidden.dtype).replace("torch.", "") != _ACT_TORCH.get(info["act_dtype"]):
+        raise ValueError(f"ctx_hidden is {ctx_hidden.dtype}, the pack's activation dtype is "
+                         f"{_ACT_TORCH.get(info['act_dtype'])}")
+    if ctx_hidden.shape[1] != info["hidden"]:
+        raise ValueError(f"ctx_hidden has {ctx_hidden.shape[1]} columns, the pack {info['hidden']}")
+    dev = ctx_hidden.device
     T = ctx_hidden.shape[0]
-    W = 0 if commit_lens is None else int(locs_row_width)
-    B = 0 if commit_lens is None else commit_lens.numel()
-    st, reason = ctx_kv_write_raw(
+    _check_index("positions", positions, T, dev)
+    _check_index("locs", locs, T, dev)
+    W, B = 0, 0
+    if commit_lens is not None:
+        W = int(locs_row_width)
+        if W <= 0 or T % W:
+            raise ValueError("locs_row_width must be positive and divide the row count")
+        B = T // W
+        _check_index("commit_lens", commit_lens, B, dev)
+    if range_errors is not None:
+        _check_index("range_errors", range_errors, 1, dev)
+    need = pack.workspace_bytes(T, commit_lens is not None)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None and workspace.device != dev:
+        raise ValueError(f"workspace is on {workspace.device}, expected {dev}")
+    st, detail = ctx_kv_write_raw(
         pack, ctx_hidden.data_ptr(), T, ctx_hidden.stride(0), positions.data_ptr(),
         locs.data_ptr(), None if commit_lens is None else commit_lens.data_ptr(), W, B, pools,
-        stream)
+        stream, None if workspace is None else workspace.data_ptr(),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        None if range_errors is None else range_errors.data_ptr(),
+        WRITE_VALIDATE if validate else 0)
     if st == FALLBACK:
         return False
+    if st == E_RANGE:
+        raise RangeError(detail, f"dspark_ctx_kv_write: {range_str(detail)}")
     _raise_for(st, "dspark_ctx_kv_write")
     return True
 
@@ -345,9 +462,26 @@ def table_qk_norm_rope(qkv, positions, q_norm_weight, k_norm_weight, cos_sin_cac
     """Enqueue the in-place QK norm + rotation on ``qkv`` [T, row_stride]. True
     when enqueued, False on fallback (nothing changed); ValueError on misuse.
     ``range_errors`` is an optional int64 device tensor of one element that
-    counts tokens skipped for a position outside the table."""
+    counts tokens skipped for a position outside the table. ValueError also for
+    positions that are not a contiguous int64 tensor of T entries, a table that
+    is not a contiguous fp32 [P, head_dim] tensor, norm weights of fewer than
+    head_dim contiguous entries, or tensors on another device."""
+    import torch
     if qkv.dim() != 2 or qkv.stride(1) != 1:
         raise ValueError("qkv must be [T, row_stride] with unit column stride")
+    dev = qkv.device
+    _check_index("positions", positions, qkv.shape[0], dev)
+    if range_errors is not None:
+        _check_index("range_errors", range_errors, 1, dev)
+    if (cos_sin_cache.dtype != torch.float32 or cos_sin_cache.dim() != 2
+            or cos_sin_cache.shape[1] != head_dim or not cos_sin_cache.is_contiguous()
+            or cos_sin_cache.device != dev):
+        raise ValueError("cos_sin_cache must be a contiguous fp32 [max_position, head_dim] "
+                         "tensor on qkv's device")
+    for name, w in (("q_norm_weight", q_norm_weight), ("k_norm_weight", k_norm_weight)):
+        if w.numel() < head_dim or not w.is_contiguous() or w.device != dev:
+            raise ValueError(f"{name} must be a contiguous tensor of head_dim entries on "
+                             "qkv's device")
     st, reason = table_qk_norm_rope_raw(
         qkv.data_ptr(), qkv.shape[0], qkv.stride(0), positions.data_ptr(), num_q_heads,
         num_k_heads, head_dim, _dtype_code(qkv), q_norm_weight.data_ptr(),

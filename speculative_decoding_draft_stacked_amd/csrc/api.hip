@@ -1,11 +1,16 @@
-// C ABI of the context-KV write library: eligibility, pack, write, strings.
+// C ABI of the context-KV write library: eligibility, pack, plan, write, strings.
 //
 // Eligibility follows the fast-path-or-fallback pattern of sglang PR #31986
 // ("_stacked_ctx_kv_params": sliceable weights, equal eps, consistent bias) and
 // sglang PR #31847 ("_build_fused_kv_write_bundle": no K/V scale, equal head
 // shape, neox full-dim rotary over one shared table, pool dtype and head-major
-// layout). Every reason is reported instead of falling back silently.
+// layout). Every reason is reported instead of falling back silently, and with
+// DSPARK_LOG set it is also printed.
+#include <atomic>
+#include <cstdio>
+#include <cstdlib>
 #include <new>
+#include <vector>
 
 #include "internal.h"
 
@@ -24,11 +29,8 @@ struct dspark_ctx_kv_pack {
   float* knw;                // [L, head_dim]
   const float* table;        // [P, head_dim], caller-owned
   int64_t table_rows;
-  unsigned long long* err;   // range error counter
   uint16_t* zeros;           // 256 zero bytes read by out-of-range K lanes
-  float* part;               // K-split workspace of the write (part_cap floats) or nullptr
-  int64_t part_cap;
-  int* rowmap;               // committed-row map of the K-split form
+  mutable std::atomic<bool> logged_fallback{false};  // DSPARK_LOG: first write fallback printed
 };
 
 namespace {
@@ -42,18 +44,31 @@ int fallback(int32_t* out, int32_t r) {
   return DSPARK_FALLBACK;
 }
 
-bool is_act_dtype(int32_t d) { return d == DSPARK_BF16 || d == DSPARK_FP16; }
+// DSPARK_LOG set to a non-empty value other than "0" (read on fallback and
+// error paths only).
+bool log_enabled() {
+  const char* v = std::getenv("DSPARK_LOG");
+  return v && v[0] && !(v[0] == '0' && v[1] == 0);
+}
 
 void free_pack(dspark_ctx_kv_pack* p) {
   if (!p) return;
   if (p->w) (void)hipFree(p->w);
   if (p->bias) (void)hipFree(p->bias);
   if (p->knw) (void)hipFree(p->knw);
-  if (p->err) (void)hipFree(p->err);
   if (p->zeros) (void)hipFree(p->zeros);
-  if (p->part) (void)hipFree(p->part);
-  if (p->rowmap) (void)hipFree(p->rowmap);
   delete p;
+}
+
+int pack_fallback(int32_t* out, int32_t r) {
+  if (log_enabled())
+    std::fprintf(stderr, "dspark: dspark_pack_ctx_kv fell back: %s\n", dspark_fallback_str(r));
+  return fallback(out, r);
+}
+
+dspark::WritePlan plan_for(const dspark_ctx_kv_pack* p, int64_t T, bool has_commit) {
+  const int64_t R = (int64_t)p->num_layers * 2 * p->kv_size / 128;
+  return dspark::plan_write(T, R, p->hidden, has_commit, false, p->num_cus);
 }
 
 }  // namespace
@@ -62,38 +77,7 @@ extern "C" {
 
 int dspark_check_eligibility(const dspark_layer_desc* layers, int32_t num_layers, int64_t hidden,
                              int32_t act_dtype, int32_t* fallback_reason) {
-  set_reason(fallback_reason, DSPARK_FB_NONE);
-  if (num_layers < 0 || hidden <= 0 || (num_layers > 0 && !layers)) return DSPARK_E_INVALID;
-  if (num_layers == 0) return fallback(fallback_reason, DSPARK_FB_NO_LAYERS);
-  if (num_layers > DSPARK_MAX_LAYERS) return fallback(fallback_reason, DSPARK_FB_TOO_MANY_LAYERS);
-  if (!is_act_dtype(act_dtype)) return fallback(fallback_reason, DSPARK_FB_DTYPE);
-  const dspark_layer_desc& l0 = layers[0];
-  for (int32_t i = 0; i < num_layers; ++i) {
-    const dspark_layer_desc& d = layers[i];
-    if (!d.qkv_weight || !d.k_norm_weight) return DSPARK_E_INVALID;
-    const bool sliceable = d.w_dtype == act_dtype && d.w_col_stride == 1 && d.q_size >= 0 &&
-                           d.kv_size > 0 && d.w_rows >= d.q_size + 2 * d.kv_size &&
-                           d.w_row_stride >= hidden;
-    if (!sliceable) return fallback(fallback_reason, DSPARK_FB_NOT_SLICEABLE);
-    if (d.k_norm_eps != l0.k_norm_eps) return fallback(fallback_reason, DSPARK_FB_EPS_MISMATCH);
-    if (d.has_kv_scale) return fallback(fallback_reason, DSPARK_FB_KV_SCALE);
-    if (d.head_dim != l0.head_dim || d.kv_size != l0.kv_size)
-      return fallback(fallback_reason, DSPARK_FB_SHAPE);
-    if (!d.rope_is_neox || d.rope_dim != d.head_dim || d.rope_dtype != DSPARK_FP32 ||
-        !d.rope_cos_sin || d.rope_max_pos <= 0 || d.rope_max_pos != l0.rope_max_pos)
-      return fallback(fallback_reason, DSPARK_FB_ROPE);
-    if (d.k_norm_dtype != DSPARK_BF16 && d.k_norm_dtype != DSPARK_FP16 &&
-        d.k_norm_dtype != DSPARK_FP32)
-      return fallback(fallback_reason, DSPARK_FB_DTYPE);
-  }
-  for (int32_t i = 0; i < num_layers; ++i)
-    if ((layers[i].qkv_bias != nullptr) != (l0.qkv_bias != nullptr))
-      return fallback(fallback_reason, DSPARK_FB_MIXED_BIAS);
-  const int64_t D = l0.head_dim;
-  if ((D != 64 && D != 128) || l0.kv_size % D != 0 || hidden % 8 != 0 ||
-      l0.w_row_stride % 8 != 0)
-    return fallback(fallback_reason, DSPARK_FB_SHAPE);
-  return DSPARK_OK;
+  return dspark::check_layers(layers, num_layers, hidden, act_dtype, fallback_reason);
 }
 
 int dspark_pack_ctx_kv(const dspark_layer_desc* layers, int32_t num_layers, int64_t hidden,
@@ -101,13 +85,16 @@ int dspark_pack_ctx_kv(const dspark_layer_desc* layers, int32_t num_layers, int6
                        int32_t* fallback_reason) {
   if (!out) return DSPARK_E_INVALID;
   *out = nullptr;
-  const int st = dspark_check_eligibility(layers, num_layers, hidden, act_dtype, fallback_reason);
+  int32_t reason = DSPARK_FB_NONE;
+  const int st = dspark::check_layers(layers, num_layers, hidden, act_dtype, &reason);
+  set_reason(fallback_reason, reason);
+  if (st == DSPARK_FALLBACK) return pack_fallback(fallback_reason, reason);
   if (st != DSPARK_OK) return st;
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   for (int32_t i = 0; i < num_layers; ++i) {
     // 16-byte vector reads of every weight row need an aligned base
     if (reinterpret_cast<uintptr_t>(layers[i].qkv_weight) % 16 != 0)
-      return fallback(fallback_reason, DSPARK_FB_NOT_SLICEABLE);
+      return pack_fallback(fallback_reason, DSPARK_FB_NOT_SLICEABLE);
   }
 
   dspark_ctx_kv_pack* p = new (std::nothrow) dspark_ctx_kv_pack();
@@ -134,7 +121,6 @@ int dspark_pack_ctx_kv(const dspark_layer_desc* layers, int32_t num_layers, int6
   const int64_t nk = (hidden + 63) / 64;
   int* differ = nullptr;
   uint16_t* plain = nullptr;
-  int status = DSPARK_OK;
   auto fail = [&](int s) {
     if (differ) (void)hipFree(differ);
     if (plain) (void)hipFree(plain);
@@ -147,17 +133,8 @@ int dspark_pack_ctx_kv(const dspark_layer_desc* layers, int32_t num_layers, int6
     return fail(DSPARK_E_NOMEM);
   if (hipMalloc(&p->knw, (size_t)(num_layers * l0.head_dim * 4)) != hipSuccess)
     return fail(DSPARK_E_NOMEM);
-  if (hipMalloc(&p->err, sizeof(unsigned long long)) != hipSuccess) return fail(DSPARK_E_NOMEM);
   if (hipMalloc(&p->zeros, 256) != hipSuccess) return fail(DSPARK_E_NOMEM);
   if (hipMalloc(&differ, sizeof(int)) != hipSuccess) return fail(DSPARK_E_NOMEM);
-  // workspace of the write's K-split form, used when the weight has few
-  // 128-row tiles for the device (at most one workgroup per compute unit)
-  if (n_tot / 128 * 2 <= p->num_cus) {
-    p->part_cap = (int64_t)p->num_cus * dspark::kPartFloatsPerCU;
-    if (hipMalloc(&p->part, (size_t)p->part_cap * 4) != hipSuccess ||
-        hipMalloc(&p->rowmap, dspark::kRowMapInts * sizeof(int)) != hipSuccess)
-      return fail(DSPARK_E_NOMEM);
-  }
 
   bool ok = true;
   for (int32_t l = 0; l < num_layers && ok; ++l) {
@@ -173,7 +150,6 @@ int dspark_pack_ctx_kv(const dspark_layer_desc* layers, int32_t num_layers, int6
                                       l0.head_dim, stream) == hipSuccess;
   }
   ok = ok && dspark::launch_block_weight(plain, n_tot, hidden, p->w, stream) == hipSuccess;
-  ok = ok && hipMemsetAsync(p->err, 0, sizeof(unsigned long long), stream) == hipSuccess;
   ok = ok && hipMemsetAsync(p->zeros, 0, 256, stream) == hipSuccess;
   ok = ok && hipMemsetAsync(differ, 0, sizeof(int), stream) == hipSuccess;
   for (int32_t l = 1; l < num_layers && ok; ++l) {
@@ -187,9 +163,8 @@ int dspark_pack_ctx_kv(const dspark_layer_desc* layers, int32_t num_layers, int6
   ok = ok && hipStreamSynchronize(stream) == hipSuccess;
   if (!ok) return fail(DSPARK_E_DEVICE);
   if (h_differ) {
-    status = fail(DSPARK_FALLBACK);
-    set_reason(fallback_reason, DSPARK_FB_ROPE);
-    return status;
+    fail(DSPARK_FALLBACK);
+    return pack_fallback(fallback_reason, DSPARK_FB_ROPE);
   }
   (void)hipFree(differ);
   (void)hipFree(plain);
@@ -197,19 +172,74 @@ int dspark_pack_ctx_kv(const dspark_layer_desc* layers, int32_t num_layers, int6
   return DSPARK_OK;
 }
 
-int dspark_ctx_kv_write(const dspark_ctx_kv_pack* p, const void* ctx_hidden, int64_t num_tokens,
-                        int64_t hidden_row_stride, const int64_t* positions, const int64_t* locs,
-                        const int64_t* commit_lens, int64_t locs_row_width, int64_t num_requests,
-                        const dspark_pool_desc* pools, int32_t num_pools, void* stream_ptr,
-                        int32_t* fallback_reason) {
-  set_reason(fallback_reason, DSPARK_FB_NONE);
+int dspark_ctx_kv_plan(const dspark_ctx_kv_pack* p, int64_t num_tokens, int32_t has_commit,
+                       dspark_write_plan* plan) {
+  if (!p || !plan || num_tokens < 0) return DSPARK_E_INVALID;
+  const dspark::WritePlan w = plan_for(p, num_tokens, has_commit != 0);
+  plan->kernel = w.kernel;
+  plan->token_tile = w.kernel == dspark::kKernelTiled ? w.bt : 32 * w.nb;
+  plan->workgroups = w.grid;
+  plan->reduce_workgroups = w.reduce_grid;
+  plan->k_parts = w.ksplits;
+  plan->compacts = w.compacts ? 1 : 0;
+  plan->workspace_bytes = dspark::plan_workspace_bytes(w);
+  return DSPARK_OK;
+}
+
+int dspark_ctx_kv_workspace_bytes(const dspark_ctx_kv_pack* p, int64_t num_tokens,
+                                  int32_t has_commit, int64_t* bytes) {
+  if (!p || !bytes || num_tokens < 0) return DSPARK_E_INVALID;
+  *bytes = dspark::plan_workspace_bytes(plan_for(p, num_tokens, has_commit != 0));
+  return DSPARK_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Validate mode: the index arrays to the host (synchronising `stream`) and the
+// row checks. DSPARK_OK, DSPARK_E_RANGE (cause in *detail) or DSPARK_E_DEVICE.
+int validate_rows(const dspark_ctx_kv_pack* p, const dspark::WriteArgs& a, int64_t num_requests,
+                  hipStream_t stream, int32_t* detail) {
+  const int64_t T = a.T;
+  std::vector<int64_t> pos((size_t)T), locs((size_t)T), commit((size_t)num_requests);
+  bool ok = hipMemcpyAsync(pos.data(), a.pos, (size_t)T * 8, hipMemcpyDeviceToHost, stream) ==
+                hipSuccess &&
+            hipMemcpyAsync(locs.data(), a.locs, (size_t)T * 8, hipMemcpyDeviceToHost, stream) ==
+                hipSuccess;
+  if (ok && a.commit)
+    ok = hipMemcpyAsync(commit.data(), a.commit, (size_t)num_requests * 8, hipMemcpyDeviceToHost,
+                        stream) == hipSuccess;
+  ok = ok && hipStreamSynchronize(stream) == hipSuccess;
+  if (!ok) return DSPARK_E_DEVICE;
+  int32_t cause = DSPARK_RANGE_NONE;
+  int64_t row = -1;
+  const int st = dspark::check_rows(pos.data(), locs.data(), a.commit ? commit.data() : nullptr,
+                                    T, a.W, a.P, a.slots, p->num_layers, &cause, &row);
+  if (st == DSPARK_E_RANGE) {
+    set_reason(detail, cause);
+    if (log_enabled())
+      std::fprintf(stderr, "dspark: dspark_ctx_kv_write validate: row %lld: %s\n",
+                   (long long)row, dspark_range_str(cause));
+  }
+  return st;
+}
+
+// Shared body of the write entry points: checks, the args, the plan, launch.
+int write_impl(const dspark_ctx_kv_pack* p, const void* ctx_hidden, int64_t num_tokens,
+               int64_t hidden_row_stride, const int64_t* positions, const int64_t* locs,
+               const int64_t* commit_lens, int64_t locs_row_width, int64_t num_requests,
+               const dspark_pool_desc* pools, int32_t num_pools, void* workspace,
+               int64_t workspace_bytes, unsigned long long* range_errors, uint32_t flags,
+               void* stream_ptr, int32_t* detail) {
+  set_reason(detail, DSPARK_FB_NONE);
   if (!p || num_tokens < 0) return DSPARK_E_INVALID;
   // commit_lens and the window width come together (sglang PR #31847,
   // "fused_kv_norm_rope_write": ValueError otherwise)
   const bool has_commit = commit_lens != nullptr;
-  if (has_commit != (locs_row_width > 0)) return DSPARK_E_INVALID;
-  if (has_commit && num_requests * locs_row_width != num_tokens) return DSPARK_E_INVALID;
-  if (!has_commit && (locs_row_width != 0 || num_requests != 0)) return DSPARK_E_INVALID;
+  if (!dspark::write_window_ok(has_commit, num_tokens, locs_row_width, num_requests))
+    return DSPARK_E_INVALID;
+  if (flags & ~(uint32_t)DSPARK_WRITE_VALIDATE) return DSPARK_E_INVALID;
   if (!pools || num_pools != p->num_layers) return DSPARK_E_INVALID;
   if (num_tokens == 0) return DSPARK_OK;
   if (!ctx_hidden || !positions || !locs) return DSPARK_E_INVALID;
@@ -226,31 +256,36 @@ int dspark_ctx_kv_write(const dspark_ctx_kv_pack* p, const void* ctx_hidden, int
   for (int32_t l = 0; l < p->num_layers; ++l) {
     const dspark_pool_desc& q = pools[l];
     if (!q.k || !q.v || q.num_slots < 0) return DSPARK_E_INVALID;
-    const bool layout_ok =
-        q.dtype == p->dtype && q.k_stride1 == D && q.k_stride2 == 1 && q.v_stride1 == D &&
-        q.v_stride2 == 1 && q.k_stride0 >= NH * D && q.v_stride0 >= NH * D &&
-        q.k_stride0 % 8 == 0 && q.v_stride0 % 8 == 0 &&
-        reinterpret_cast<uintptr_t>(q.k) % 16 == 0 && reinterpret_cast<uintptr_t>(q.v) % 16 == 0;
-    if (!layout_ok) return fallback(fallback_reason, DSPARK_FB_POOL_LAYOUT);
+    if (!dspark::pool_layout_ok(q, p->dtype, NH, D)) {
+      if (log_enabled() && !p->logged_fallback.exchange(true))
+        std::fprintf(stderr, "dspark: dspark_ctx_kv_write fell back (layer %d): %s\n", (int)l,
+                     dspark_fallback_str(DSPARK_FB_POOL_LAYOUT));
+      return fallback(detail, DSPARK_FB_POOL_LAYOUT);
+    }
     a.pk[l] = static_cast<uint16_t*>(q.k);
     a.pv[l] = static_cast<uint16_t*>(q.v);
     a.ks0[l] = q.k_stride0;
     a.vs0[l] = q.v_stride0;
     a.slots[l] = q.num_slots;
   }
+  const dspark::WritePlan plan = plan_for(p, num_tokens, has_commit);
+  const int64_t need = dspark::plan_workspace_bytes(plan);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+      return DSPARK_E_INVALID;
+    a.partial = static_cast<float*>(workspace);
+    a.rowmap = reinterpret_cast<int*>(static_cast<char*>(workspace) + plan.part_floats * 4);
+  }
   a.x = static_cast<const uint16_t*>(ctx_hidden);
   a.w = p->w;
   a.bias = p->bias;
   a.knw = p->knw;
   a.zeros = p->zeros;
-  a.partial = p->part;
-  a.rowmap = p->rowmap;
-  a.part_cap = p->part_cap;
   a.table = p->table;
   a.pos = positions;
   a.locs = locs;
   a.commit = commit_lens;
-  a.err = p->err;
+  a.err = range_errors;
   a.x_stride = hidden_row_stride;
   a.T = num_tokens;
   a.P = p->table_rows;
@@ -260,10 +295,29 @@ int dspark_ctx_kv_write(const dspark_ctx_kv_pack* p, const void* ctx_hidden, int
   a.NH = (int32_t)NH;
   a.R = (int64_t)p->num_layers * 2 * p->kv_size / 128;
   a.eps = p->eps;
-  const hipError_t e = dspark::launch_ctx_kv_write(a, (int)D, p->dtype == DSPARK_FP16,
-                                                   p->has_bias != 0, has_commit, p->num_cus,
-                                                   static_cast<hipStream_t>(stream_ptr));
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  if (flags & DSPARK_WRITE_VALIDATE) {
+    const int st = validate_rows(p, a, num_requests, stream, detail);
+    if (st != DSPARK_OK) return st;
+  }
+  const hipError_t e = dspark::launch_ctx_kv_write(a, plan, (int)D, p->dtype == DSPARK_FP16,
+                                                   p->has_bias != 0, has_commit, stream);
   return e == hipSuccess ? DSPARK_OK : DSPARK_E_DEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dspark_ctx_kv_write(const dspark_ctx_kv_pack* p, const void* ctx_hidden, int64_t num_tokens,
+                        int64_t hidden_row_stride, const int64_t* positions, const int64_t* locs,
+                        const int64_t* commit_lens, int64_t locs_row_width, int64_t num_requests,
+                        const dspark_pool_desc* pools, int32_t num_pools, void* workspace,
+                        int64_t workspace_bytes, unsigned long long* range_errors, uint32_t flags,
+                        void* stream_ptr, int32_t* detail) {
+  return write_impl(p, ctx_hidden, num_tokens, hidden_row_stride, positions, locs, commit_lens,
+                    locs_row_width, num_requests, pools, num_pools, workspace, workspace_bytes,
+                    range_errors, flags, stream_ptr, detail);
 }
 
 int dspark_table_qk_norm_rope(void* qkv, int64_t num_tokens, int64_t row_stride,
@@ -336,18 +390,6 @@ int dspark_verify_accept(const int64_t* draft_tokens, int64_t draft_row_stride,
   return e == hipSuccess ? DSPARK_OK : DSPARK_E_DEVICE;
 }
 
-int dspark_pack_range_errors(const dspark_ctx_kv_pack* p, void* stream_ptr, int64_t* count) {
-  if (!p || !count) return DSPARK_E_INVALID;
-  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-  unsigned long long h = 0;
-  if (hipMemcpyAsync(&h, p->err, sizeof(h), hipMemcpyDeviceToHost, stream) != hipSuccess ||
-      hipMemsetAsync(p->err, 0, sizeof(h), stream) != hipSuccess ||
-      hipStreamSynchronize(stream) != hipSuccess)
-    return DSPARK_E_DEVICE;
-  *count = (int64_t)h;
-  return DSPARK_OK;
-}
-
 int dspark_pack_info(const dspark_ctx_kv_pack* p, int32_t* num_layers, int64_t* hidden,
                      int64_t* kv_size, int64_t* head_dim, int32_t* act_dtype, int32_t* has_bias) {
   if (!p) return DSPARK_E_INVALID;
@@ -384,6 +426,7 @@ const char* dspark_status_str(int status) {
     case DSPARK_OK: return "ok";
     case DSPARK_FALLBACK: return "fallback: not eligible for the stacked write";
     case DSPARK_E_INVALID: return "invalid argument";
+    case DSPARK_E_RANGE: return "position or slot out of range, or a slot written twice";
     case DSPARK_E_DEVICE: return "HIP runtime error";
     case DSPARK_E_NOMEM: return "device allocation failed";
     default: return "unknown status";
@@ -404,6 +447,16 @@ const char* dspark_fallback_str(int reason) {
     case DSPARK_FB_ROPE: return "rotary is not neox full-dim over one shared fp32 table";
     case DSPARK_FB_POOL_LAYOUT: return "KV pool dtype, layout or alignment unsupported";
     default: return "unknown reason";
+  }
+}
+
+const char* dspark_range_str(int cause) {
+  switch (cause) {
+    case DSPARK_RANGE_NONE: return "none";
+    case DSPARK_RANGE_POSITION: return "a stored row's position is outside the rotary table";
+    case DSPARK_RANGE_SLOT: return "a stored row's slot is past a layer's pool";
+    case DSPARK_RANGE_DUPLICATE: return "two stored rows name the same slot";
+    default: return "unknown cause";
   }
 }
 

@@ -152,7 +152,7 @@ __device__ __forceinline__ void scatter_tile(const WriteArgs& a, const uint16_t*
     const int n = is_k ? jj : jj - a.NH;
     const int64_t p = a.pos[t];
     if (p < 0 || p >= a.P || loc >= a.slots[layer]) {
-      if (j == 0 && jj == 0) atomicAdd(a.err, 1ull);  // once per (row, layer)
+      if (j == 0 && jj == 0 && a.err) atomicAdd(a.err, 1ull);  // once per (row, layer)
       continue;
     }
     const uint16_t* src = sO + tt * LDO + hd * D + j * 8;
@@ -468,8 +468,6 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
 // costs every workgroup a pass per 512 rows, so longer windows (up to 32768
 // rows reach this kernel when there are few weight tiles) keep contiguous
 // splits instead.
-constexpr int64_t kCompactMaxRows = 1024;
-
 template <int BT>
 __device__ int compact_rows(const WriteArgs& a, int64_t sp, int splits, int* map, int* wcnt,
                             int tid) {
@@ -877,130 +875,79 @@ __global__ __launch_bounds__(256) void ctx_kv_stream_reduce(const WriteArgs a, i
                                           COMMIT ? smap : nullptr);
 }
 
-template <bool FP16, int D, bool BIAS, bool COMMIT, int BT>
-hipError_t launch_tiled_bt(const WriteArgs& a, int64_t grid, int64_t t_tiles, hipStream_t stream) {
-  hipLaunchKernelGGL((ctx_kv_tiled_kernel<FP16, D, BIAS, COMMIT, BT>), dim3((uint32_t)grid),
-                     dim3(512), 0, stream, a, (int)t_tiles);
-  return hipGetLastError();
-}
-
-// Token tile of the large-T kernel: the one with the least (rounds of
-// workgroups over the device) x (tokens per tile), i.e. the shortest
-// critical path when every tile of a size costs about the same; ties go to
-// the larger tile, which needs fewer line requests per MFMA.
 template <bool FP16, int D, bool BIAS, bool COMMIT>
-hipError_t launch_tiled(const WriteArgs& a, int num_cus, hipStream_t stream) {
-  const int64_t rp = (a.R + 1) / 2;
-  int best_bt = 256;
-  int64_t best_cost = -1;
-  for (int bt : {256, 192, 128}) {
-    const int64_t grid = rp * ((a.T + bt - 1) / bt);
-    const int64_t cost = (grid + num_cus - 1) / num_cus * bt;
-    if (best_cost < 0 || cost < best_cost) best_cost = cost, best_bt = bt;
+hipError_t launch_tiled(const WriteArgs& a, const WritePlan& p, hipStream_t stream) {
+  if (p.grid <= 0 || p.grid > 0x7FFFFFFF || p.splits > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((uint32_t)p.grid), block(512);
+  const int t_tiles = (int)p.splits;
+  switch (p.bt) {
+    case 256:
+      hipLaunchKernelGGL((ctx_kv_tiled_kernel<FP16, D, BIAS, COMMIT, 256>), grid, block, 0, stream,
+                         a, t_tiles);
+      break;
+    case 192:
+      hipLaunchKernelGGL((ctx_kv_tiled_kernel<FP16, D, BIAS, COMMIT, 192>), grid, block, 0, stream,
+                         a, t_tiles);
+      break;
+    case 128:
+      hipLaunchKernelGGL((ctx_kv_tiled_kernel<FP16, D, BIAS, COMMIT, 128>), grid, block, 0, stream,
+                         a, t_tiles);
+      break;
+    default: return hipErrorInvalidValue;
   }
-  const int64_t t_tiles = (a.T + best_bt - 1) / best_bt;
-  const int64_t grid = rp * t_tiles;
-  if (grid <= 0 || grid > 0x7FFFFFFF || t_tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  switch (best_bt) {
-    case 256: return launch_tiled_bt<FP16, D, BIAS, COMMIT, 256>(a, grid, t_tiles, stream);
-    case 192: return launch_tiled_bt<FP16, D, BIAS, COMMIT, 192>(a, grid, t_tiles, stream);
-    default: return launch_tiled_bt<FP16, D, BIAS, COMMIT, 128>(a, grid, t_tiles, stream);
-  }
-}
-
-// K parts for the write's streaming kernel: where its row tiles x token
-// splits leave at least half of the device idle (few weight tiles, e.g. one
-// GPU's share of the KV heads), K is split over workgroups too, so that the
-// grid fills the device and each workgroup streams a slice of its tile; the
-// fp32 part sums then cost a second launch (ctx_kv_stream_reduce). 1: none.
-constexpr int64_t kKSplitTokenSplits = 4;
-
-int write_ksplits(const WriteArgs& a, int64_t row_tiles, int64_t splits, int nb, int num_cus) {
-  if (a.part_cap <= 0 || !a.partial || !a.rowmap || a.T > kCompactMaxRows) return 1;
-  if (row_tiles * splits * 2 > num_cus) return 1;
-  const int64_t nk_all = (a.H + BK - 1) / BK;
-  int64_t ks = num_cus / (row_tiles * splits);
-  if (ks > nk_all / 8) ks = nk_all / 8;  // at least 8 chunks of 64 per part
-  if (ks > 16) ks = 16;
-  if (ks < 2 || splits * 32 * nb > kRowMapInts ||
-      ks * row_tiles * splits * 32 * nb * BN > a.part_cap)
-    return 1;
-  return (int)ks;
+  return hipGetLastError();
 }
 
 template <bool FP16, int D, bool BIAS, bool COMMIT, int NB>
-hipError_t launch_stream_nb(const WriteArgs& a, int64_t row_tiles, int splits, int num_cus,
-                            hipStream_t stream) {
-  const int ks = D == kRowsOut ? 1 : write_ksplits(a, row_tiles, splits, NB, num_cus);
-  if (ks > 1) {
-    WriteArgs b = a;
-    b.ksplits = ks;
-    hipLaunchKernelGGL((ctx_kv_stream_kernel<FP16, D, BIAS, COMMIT, NB>),
-                       dim3((uint32_t)((row_tiles * ks + 7) / 8 * 8 * splits)), dim3(512), 0, stream,
-                       b, splits);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if constexpr (D != kRowsOut)
-      hipLaunchKernelGGL((ctx_kv_stream_reduce<FP16, D, BIAS, COMMIT, NB>),
-                         dim3((uint32_t)(row_tiles * splits * NB)), dim3(256), 0, stream, b, splits);
-    return hipGetLastError();
-  }
-  hipLaunchKernelGGL((ctx_kv_stream_kernel<FP16, D, BIAS, COMMIT, NB>),
-                     dim3((uint32_t)(row_tiles * splits)), dim3(512), 0, stream, a, splits);
+hipError_t launch_stream_nb(const WriteArgs& a, const WritePlan& p, hipStream_t stream) {
+  if (p.grid <= 0 || p.grid > 0x7FFFFFFF || p.reduce_grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  WriteArgs b = a;
+  b.ksplits = p.kernel == kKernelStreamKSplit ? p.ksplits : 1;
+  hipLaunchKernelGGL((ctx_kv_stream_kernel<FP16, D, BIAS, COMMIT, NB>), dim3((uint32_t)p.grid),
+                     dim3(512), 0, stream, b, (int)p.splits);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.kernel != kKernelStreamKSplit) return e;
+  if constexpr (D != kRowsOut)
+    hipLaunchKernelGGL((ctx_kv_stream_reduce<FP16, D, BIAS, COMMIT, NB>),
+                       dim3((uint32_t)p.reduce_grid), dim3(256), 0, stream, b, (int)p.splits);
   return hipGetLastError();
 }
 
-// Small T: one round of streaming workgroups (row tiles x token splits of up
-// to 4 blocks of 32 tokens) fits on the device. Larger T: LDS-tiled kernel.
+// The plan's kernels: the LDS-tiled kernel for large T, else one round of
+// streaming workgroups (row tiles x token splits of up to 4 blocks of 32
+// tokens), with K also split over workgroups where few weight tiles would
+// leave the device idle.
 template <bool FP16, int D, bool BIAS, bool COMMIT>
-hipError_t launch_by_rows(const WriteArgs& a, int num_cus, hipStream_t stream) {
-  const int64_t row_tiles = a.R;
-  const int64_t blocks = (a.T + 31) / 32;
-  const int64_t cap = row_tiles >= num_cus ? 1 : num_cus / row_tiles;
-  if (blocks > 4 * cap) return launch_tiled<FP16, D, BIAS, COMMIT>(a, num_cus, stream);
-  int64_t splits = blocks < cap ? blocks : cap;
-  int64_t nb = (blocks + splits - 1) / splits;
-  splits = (blocks + nb - 1) / nb;
-  // With K split over workgroups as well, fewer token splits (each weight
-  // line requested by fewer workgroups) and more K parts cost less: the
-  // K-split plan takes at most kKSplitTokenSplits splits of up to 4 blocks,
-  // and is used where that plan leaves at least half of the device idle.
-  if (D != kRowsOut) {
-    int64_t s2 = splits < kKSplitTokenSplits ? splits : kKSplitTokenSplits;
-    if ((blocks + 3) / 4 > s2) s2 = (blocks + 3) / 4;
-    const int64_t nb2 = (blocks + s2 - 1) / s2;
-    s2 = (blocks + nb2 - 1) / nb2;
-    if (write_ksplits(a, row_tiles, s2, (int)nb2, num_cus) > 1) {
-      splits = s2;
-      nb = nb2;
-    }
-  }
-  switch (nb) {
-    case 1: return launch_stream_nb<FP16, D, BIAS, COMMIT, 1>(a, row_tiles, (int)splits, num_cus, stream);
-    case 2: return launch_stream_nb<FP16, D, BIAS, COMMIT, 2>(a, row_tiles, (int)splits, num_cus, stream);
-    case 3: return launch_stream_nb<FP16, D, BIAS, COMMIT, 3>(a, row_tiles, (int)splits, num_cus, stream);
-    default: return launch_stream_nb<FP16, D, BIAS, COMMIT, 4>(a, row_tiles, (int)splits, num_cus, stream);
+hipError_t launch_plan(const WriteArgs& a, const WritePlan& p, hipStream_t stream) {
+  if (p.kernel == kKernelTiled) return launch_tiled<FP16, D, BIAS, COMMIT>(a, p, stream);
+  switch (p.nb) {
+    case 1: return launch_stream_nb<FP16, D, BIAS, COMMIT, 1>(a, p, stream);
+    case 2: return launch_stream_nb<FP16, D, BIAS, COMMIT, 2>(a, p, stream);
+    case 3: return launch_stream_nb<FP16, D, BIAS, COMMIT, 3>(a, p, stream);
+    case 4: return launch_stream_nb<FP16, D, BIAS, COMMIT, 4>(a, p, stream);
+    default: return hipErrorInvalidValue;
   }
 }
 
 template <bool FP16, int D, bool BIAS>
-hipError_t launch_commit(const WriteArgs& a, bool has_commit, int num_cus, hipStream_t stream) {
-  return has_commit ? launch_by_rows<FP16, D, BIAS, true>(a, num_cus, stream)
-                    : launch_by_rows<FP16, D, BIAS, false>(a, num_cus, stream);
+hipError_t launch_commit(const WriteArgs& a, const WritePlan& p, bool has_commit,
+                         hipStream_t stream) {
+  return has_commit ? launch_plan<FP16, D, BIAS, true>(a, p, stream)
+                    : launch_plan<FP16, D, BIAS, false>(a, p, stream);
 }
 
 template <bool FP16, int D>
-hipError_t launch_bias(const WriteArgs& a, bool has_bias, bool has_commit, int num_cus,
+hipError_t launch_bias(const WriteArgs& a, const WritePlan& p, bool has_bias, bool has_commit,
                        hipStream_t stream) {
-  return has_bias ? launch_commit<FP16, D, true>(a, has_commit, num_cus, stream)
-                  : launch_commit<FP16, D, false>(a, has_commit, num_cus, stream);
+  return has_bias ? launch_commit<FP16, D, true>(a, p, has_commit, stream)
+                  : launch_commit<FP16, D, false>(a, p, has_commit, stream);
 }
 
 template <bool FP16>
-hipError_t launch_dim(const WriteArgs& a, int head_dim, bool has_bias, bool has_commit,
-                      int num_cus, hipStream_t stream) {
-  if (head_dim == 128) return launch_bias<FP16, 128>(a, has_bias, has_commit, num_cus, stream);
-  if (head_dim == 64) return launch_bias<FP16, 64>(a, has_bias, has_commit, num_cus, stream);
+hipError_t launch_dim(const WriteArgs& a, const WritePlan& p, int head_dim, bool has_bias,
+                      bool has_commit, hipStream_t stream) {
+  if (head_dim == 128) return launch_bias<FP16, 128>(a, p, has_bias, has_commit, stream);
+  if (head_dim == 64) return launch_bias<FP16, 64>(a, p, has_bias, has_commit, stream);
   return hipErrorInvalidValue;
 }
 
@@ -1008,7 +955,7 @@ hipError_t launch_dim(const WriteArgs& a, int head_dim, bool has_bias, bool has_
 
 hipError_t launch_rows_out(const WriteArgs& a, bool is_fp16, int num_cus, hipStream_t stream) {
   if (num_cus < 1) num_cus = 1;
-  if (a.ksplits > 1) {  // 128-token tiles x K parts (see producer_plan)
+  if (a.ksplits > 1) {  // 128-token tiles x K parts (see producer_ksplits)
     const int64_t splits = (a.T + 127) / 128;
     const int64_t grid = a.R * splits * a.ksplits;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
@@ -1020,34 +967,15 @@ hipError_t launch_rows_out(const WriteArgs& a, bool is_fp16, int num_cus, hipStr
                          dim3((uint32_t)grid), dim3(512), 0, stream, a, (int)splits);
     return hipGetLastError();
   }
-  return is_fp16 ? launch_by_rows<true, kRowsOut, false, false>(a, num_cus, stream)
-                 : launch_by_rows<false, kRowsOut, false, false>(a, num_cus, stream);
+  const WritePlan p = plan_write(a.T, a.R, a.H, false, true, num_cus);
+  return is_fp16 ? launch_plan<true, kRowsOut, false, false>(a, p, stream)
+                 : launch_plan<false, kRowsOut, false, false>(a, p, stream);
 }
 
-int producer_ksplits(int64_t T, int64_t R, int64_t in_features, int64_t out_features,
-                     int num_cus) {
-  // Split K only where the write kernels' small-T path would run (so that the
-  // grid is one round) and 128-token tiles alone leave the device
-  // under-filled; the row norm then holds a row in registers (<= 8192 features,
-  // a multiple of 512: four waves of whole 128-feature passes).
-  if (num_cus < 1) num_cus = 1;
-  const int64_t cap = R >= num_cus ? 1 : num_cus / R;
-  const int64_t blocks32 = (T + 31) / 32;
-  if (blocks32 > 4 * cap || out_features > 8192 || out_features % 512 != 0) return 1;
-  const int64_t tiles = R * ((T + 127) / 128);
-  if (tiles >= num_cus) return 1;
-  int64_t ks = num_cus / tiles;
-  const int64_t nk = (in_features + 63) / 64;
-  if (ks > nk / 8) ks = nk / 8;  // at least 8 chunks of 64 per part
-  if (ks > 16) ks = 16;
-  return ks < 2 ? 1 : (int)ks;
-}
-
-hipError_t launch_ctx_kv_write(const WriteArgs& a, int head_dim, bool is_fp16, bool has_bias,
-                               bool has_commit, int num_cus, hipStream_t stream) {
-  if (num_cus < 1) num_cus = 1;
-  return is_fp16 ? launch_dim<true>(a, head_dim, has_bias, has_commit, num_cus, stream)
-                 : launch_dim<false>(a, head_dim, has_bias, has_commit, num_cus, stream);
+hipError_t launch_ctx_kv_write(const WriteArgs& a, const WritePlan& plan, int head_dim,
+                               bool is_fp16, bool has_bias, bool has_commit, hipStream_t stream) {
+  return is_fp16 ? launch_dim<true>(a, plan, head_dim, has_bias, has_commit, stream)
+                 : launch_dim<false>(a, plan, head_dim, has_bias, has_commit, stream);
 }
 
 }  // namespace dspark

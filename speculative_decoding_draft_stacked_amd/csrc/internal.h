@@ -5,16 +5,11 @@
 #include <stdint.h>
 
 #include "../../include/dspark.h"
+#include "host_logic.h"
 
 namespace dspark {
 
 constexpr int kMaxLayers = DSPARK_MAX_LAYERS;
-
-// Workspace the pack owns for the write's K-split form (few weight tiles):
-// fp32 part sums of at most one workgroup per compute unit, each at most a
-// 128-row x 128-token tile, and the committed-row map of the token splits.
-constexpr int64_t kPartFloatsPerCU = 128 * 128;
-constexpr int kRowMapInts = 2048;
 
 // Everything the fused write kernel reads, passed by value in the kernel
 // arguments so that one launch can address every layer's pool.
@@ -28,12 +23,11 @@ struct WriteArgs {
   const int64_t* pos;       // [T]
   const int64_t* locs;      // [T]
   const int64_t* commit;    // [T / W] or nullptr
-  unsigned long long* err;  // range error counter
+  unsigned long long* err;  // range error counter or nullptr
   uint16_t* y;              // producer only: [T, R * 128] output rows (row stride y_stride)
   float* partial;           // producer: [R, T] sums of squares per 128-feature group;
-                            // write: the pack's fp32 K-part workspace (part_cap floats)
-  int* rowmap;              // write: the pack's committed-row map (kRowMapInts ints)
-  int64_t part_cap;         // write: floats in `partial` (0: no K split)
+                            // write: fp32 K-part sums of the caller's workspace
+  int* rowmap;              // write: committed-row map of the caller's workspace
   int64_t y_stride;
   int64_t R;                // 128-row tiles of the blocked weight
   int32_t ksplits;          // K parts over workgroups (<= 1: none); set by the launchers
@@ -92,12 +86,9 @@ hipError_t launch_verify_accept(const VerifyArgs& a, hipStream_t stream);
 
 // Launches the context producer's GEMM for `a` (x = aux hidden, w = blocked
 // projection weight with a.R row tiles, H = input features): rounded outputs
-// to a.y and per-(128-feature group, token) sums of squares to a.partial.
+// to a.y and per-(128-feature group, token) sums of squares to a.partial, or,
+// with a.ksplits > 1, fp32 partial projections to a.partial.
 hipError_t launch_rows_out(const WriteArgs& a, bool is_fp16, int num_cus, hipStream_t stream);
-
-// K parts the producer's projection is split into for these sizes (1: none).
-int producer_ksplits(int64_t T, int64_t R, int64_t in_features, int64_t out_features,
-                     int num_cus);
 
 // Launches the row RMSNorm that completes the producer. With ksplits <= 1, y
 // holds the rounded projection and `partial` the [groups, T] group sums of
@@ -137,11 +128,12 @@ struct AttnArgs {
 hipError_t launch_draft_attention(const AttnArgs& a, int head_dim, bool is_fp16,
                                   hipStream_t stream);
 
-// Launches the fused GEMM + norm + rotation + scatter for `a` on `stream`.
-// `num_cus` (compute units of the device) sizes the small-T grid. Shapes have
-// been validated by the caller. Returns the launch status.
-hipError_t launch_ctx_kv_write(const WriteArgs& a, int head_dim, bool is_fp16, bool has_bias,
-                               bool has_commit, int num_cus, hipStream_t stream);
+// Launches the fused GEMM + norm + rotation + scatter for `a` on `stream`
+// following `plan` (plan_write for a.T, a.R, a.H). Shapes and the workspace
+// (a.partial, a.rowmap for the K-split plan) have been validated by the
+// caller. Returns the launch status.
+hipError_t launch_ctx_kv_write(const WriteArgs& a, const WritePlan& plan, int head_dim,
+                               bool is_fp16, bool has_bias, bool has_commit, hipStream_t stream);
 
 // Pack helpers.
 hipError_t launch_widen_to_f32(const void* src, int dtype, float* dst, int64_t n,

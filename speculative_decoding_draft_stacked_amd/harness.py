@@ -46,6 +46,7 @@ class DeviceCase:
         self.locs = torch.from_numpy(case.locs).cuda()
         self.commit = None if case.commit_lens is None else torch.from_numpy(case.commit_lens).cuda()
         self.pool_row_pad = pool_row_pad
+        self.err = torch.zeros(1, dtype=torch.int64, device="cuda")  # range-error counter
         self.reset_pools()
 
     def reset_pools(self):
@@ -76,11 +77,27 @@ class DeviceCase:
         assert p is not None, dk.fallback_str(dk.last_fallback_reason)
         return p
 
-    def write(self, pack) -> bool:
+    def workspace(self, pack):
+        """A device workspace of the size the write needs (None when it needs none)."""
+        n = pack.workspace_bytes(self.case.T, self.commit is not None)
+        return torch.empty(n, dtype=torch.uint8, device="cuda") if n else None
+
+    def write(self, pack, workspace=None, validate: bool = False) -> bool:
         c = self.case
         return dk.ctx_kv_write(pack, self.x, self.positions, self.locs, self.pool_descs(),
                                commit_lens=self.commit,
-                               locs_row_width=c.row_width if self.commit is not None else None)
+                               locs_row_width=c.row_width if self.commit is not None else None,
+                               workspace=workspace if workspace is not None
+                               else self.workspace(pack),
+                               range_errors=self.err, validate=validate)
+
+    def range_errors(self) -> int:
+        """Reads and clears the count of rows skipped for an out-of-range
+        position or slot (per row and layer)."""
+        torch.cuda.synchronize()
+        n = int(self.err.item())
+        self.err.zero_()
+        return n
 
     def pools_host(self):
         torch.cuda.synchronize()

@@ -70,3 +70,34 @@ def test_recorded_traffic_only_for_the_current_source(tmp_path, monkeypatch):
     assert bench.measured_traffic("decode_commit") == 123
     assert bench.measured_traffic("prefill_8k") is None  # taken on another source
     assert bench.measured_traffic("wide_gqa_d64") is None  # never recorded
+
+
+def test_executed_work_follows_the_plan():
+    """Compacted commit windows project only the stored rows: the executed
+    FLOPs (and so the roofline's bound) use those rows; bytes are unchanged."""
+    c = _decode_commit_like()
+    alg = bench.algorithmic(c, 158)
+    exe = bench.executed(c, 158, {"compacts": True})
+    assert exe["rows"] == 158 and exe["flops"] == 2 * 158 * 10240 * 4096
+    assert exe["bytes"] == alg["bytes"]
+    assert bench.executed(c, 158, {"compacts": False})["flops"] == alg["flops"]
+    # wide_gqa_d64's shape: the method's count is above the ridge (MFMA), the
+    # executed work below it (HBM)
+    wide = types.SimpleNamespace(T=512, H=7168, n_tot=5120, qkv_b=None, L=5, D=64,
+                                 num_requests=64)
+    m = bench.algorithmic(wide, 276)
+    e = bench.executed(wide, 276, {"compacts": True})
+    assert bench.roofline(m, 50e-6, "none")["bound"] == "mfma"
+    assert bench.roofline(e, 50e-6, "none")["bound"] == "hbm"
+
+
+def test_spread_percentiles():
+    p = bench.percentiles([1.0, 2.0, 3.0, 4.0, 5.0])
+    assert p["us_median"] == 3000.0 and p["replays"] == 5
+    assert p["us_p10"] == 1400.0 and p["us_p90"] == 4600.0
+
+
+def test_default_run_is_every_write_config_with_prefill_headline():
+    assert bench.HEADLINE == "prefill_8k" and bench.HEADLINE in bench.WRITE_CONFIGS
+    assert {"tiny", "decode_commit", "prefill_8k", "biased_fp16",
+            "wide_gqa_d64"} <= set(bench.WRITE_CONFIGS)

@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -33,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 def test_struct_layouts_match_c(tmp_path):
     """The ctypes mirrors have the C compiler's size and field offsets."""
     fields = {"dspark_layer_desc": dk.LayerDesc, "dspark_pool_desc": dk.PoolDesc,
-              "dspark_attn_desc": dk.AttnDesc}
+              "dspark_attn_desc": dk.AttnDesc, "dspark_write_plan": dk.WritePlan}
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "dspark.h"', "int main(void) {"]
     for cname, py in fields.items():
         lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
@@ -56,8 +57,12 @@ def test_struct_layouts_match_c(tmp_path):
 def test_status_and_reason_strings():
     assert dk.status_str(dk.OK) == "ok"
     assert "fallback" in dk.status_str(dk.FALLBACK)
+    assert "out of range" in dk.status_str(dk.E_RANGE)
     assert dk.fallback_str(5) == "QKV bias present in some layers only"
     assert dk.fallback_str(1234) == "unknown reason"
+    assert "same slot" in dk.range_str(dk.RANGE_DUPLICATE)
+    assert "rotary table" in dk.range_str(dk.RANGE_POSITION)
+    assert dk.range_str(99) == "unknown cause"
 
 
 # Fake (never dereferenced) device addresses, 16-byte aligned.
@@ -131,10 +136,12 @@ def test_invalid_arguments():
     out = ctypes.c_void_p(123)
     # NULL out pointer, and NULL pack for every pack-taking call
     assert lib.dspark_pack_ctx_kv(None, 1, 256, dk.BF16, None, None, None) == dk.E_INVALID
-    assert lib.dspark_ctx_kv_write(None, None, 4, 256, None, None, None, 0, 0, None, 0, None,
-                                   None) == dk.E_INVALID
+    assert lib.dspark_ctx_kv_write(None, None, 4, 256, None, None, None, 0, 0, None, 0, None, 0,
+                                   None, 0, None, None) == dk.E_INVALID
     n = ctypes.c_int64()
-    assert lib.dspark_pack_range_errors(None, None, ctypes.byref(n)) == dk.E_INVALID
+    plan = dk.WritePlan()
+    assert lib.dspark_ctx_kv_plan(None, 4, 0, ctypes.byref(plan)) == dk.E_INVALID
+    assert lib.dspark_ctx_kv_workspace_bytes(None, 4, 0, ctypes.byref(n)) == dk.E_INVALID
     assert lib.dspark_pack_info(None, None, None, None, None, None, None) == dk.E_INVALID
     lib.dspark_pack_free(None)  # no-op
     # ineligible layers: pack reports fallback before touching the device
@@ -143,6 +150,32 @@ def test_invalid_arguments():
     assert lib.dspark_pack_ctx_kv(arr, 2, 256, dk.BF16, None, ctypes.byref(out),
                                   ctypes.byref(reason)) == dk.FALLBACK
     assert out.value is None and reason.value == 4
+
+
+_LOG_SNIPPET = r"""
+import ctypes, sys
+sys.path.insert(0, {root!r})
+import speculative_decoding_draft_stacked_amd as dk
+from tests.test_boundary_cpu import _layer
+out, reason = ctypes.c_void_p(0), ctypes.c_int32()
+arr = (dk.LayerDesc * 2)(_layer(0), _layer(1, qkv_bias=0x40000000))
+st = dk.lib().dspark_pack_ctx_kv(arr, 2, 256, dk.BF16, None, ctypes.byref(out),
+                                 ctypes.byref(reason))
+print(st, reason.value)
+"""
+
+
+@pytest.mark.parametrize("value,logged", [("1", True), ("0", False), ("", False)])
+def test_pack_fallback_logging(value, logged):
+    """DSPARK_LOG set (not "0") prints the reason of a pack fallback on stderr;
+    the pages name silent fallback as a risk."""
+    env = dict(os.environ, DSPARK_LOG=value)
+    r = subprocess.run([sys.executable, "-c", _LOG_SNIPPET.format(root=ROOT)], env=env,
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split() == [str(dk.FALLBACK), "5"]
+    line = "dspark: dspark_pack_ctx_kv fell back: QKV bias present in some layers only"
+    assert (line in r.stderr) == logged
 
 
 # ------------------------------------------------ in-place table QK norm + rotation

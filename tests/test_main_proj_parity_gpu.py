@@ -120,14 +120,11 @@ def test_padded_strides():
     _run(c, "padded aux and ctx rows", aux_pad=24, ctx_pad=40)
 
 
-@pytest.mark.parametrize("name,sample", [("proj_decode", None), ("proj_prefill_8k", 256)])
-def test_workloads(name, sample):
+@pytest.mark.parametrize("name", ["proj_decode", "proj_prefill_8k"])
+def test_workloads(name):
+    """Every token of the workload at its full size, element by element."""
     c = W.proj_workload(name)
-    rows = None
-    if sample:
-        rng = np.random.default_rng(3)
-        rows = np.unique(np.concatenate([rng.choice(c.T, sample, replace=False), [0, c.T - 1]]))
-    _, _, exact = _run(c, name, rows)
+    _, _, exact = _run(c, name)
     assert exact > 0.9  # diagnostic only; the bar is the tolerance
 
 

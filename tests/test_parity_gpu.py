@@ -37,7 +37,7 @@ def _run(case, label, rows=None, **kw):
     torch.cuda.synchronize()
     check_slot_sets(dc)
     st = compare_rows(dc, rows, label)
-    assert pack.range_errors() == 0
+    assert dc.range_errors() == 0
     say(f"  ok: {st}")
     return dc, pack, st
 
@@ -119,39 +119,42 @@ def test_k_split_form(name):
     _run(case, name)
 
 
-def test_k_split_second_call_same_pack():
-    """The K-part workspace belongs to the pack: a second, smaller call through
-    the same pack (the first 64 rows of the batch, fresh pools) writes what the
-    oracle gives for those rows."""
+def test_k_split_second_call_same_pack_and_workspace():
+    """The K-part workspace belongs to the caller: a second, smaller call
+    through the same pack and workspace (the first 64 rows of the batch, fresh
+    pools) writes what the oracle gives for those rows."""
     c1 = W.make_case(name="ks1", seed=45, T=200, H=2048, L=2, NH=1, D=128, row_width=8,
                      slots=512)
-    _, pack, _ = _run(c1, "first call")
+    dc1 = DeviceCase(c1)
+    pack = dc1.pack()
+    assert pack.plan(200, True)["kernel"] == "stream_ksplit"
+    ws = dc1.workspace(pack)
+    assert ws is not None and ws.numel() == pack.workspace_bytes(200, True)
+    say("[case] first call: T=200")
+    assert dc1.write(pack, workspace=ws)
+    torch.cuda.synchronize()
+    check_slot_sets(dc1)
+    compare_rows(dc1, None, "first call")
     c2 = dataclasses.replace(c1, name="ks2", T=64, x=c1.x[:64], positions=c1.positions[:64],
                              locs=c1.locs[:64], commit_lens=c1.commit_lens[:8])
     dc2 = DeviceCase(c2)
-    say("[case] second call through the first pack: T=64")
-    assert dc2.write(pack)
+    say("[case] second call through the first pack and workspace: T=64")
+    assert dc2.write(pack, workspace=ws)
     torch.cuda.synchronize()
     check_slot_sets(dc2)
     compare_rows(dc2, None, "second call")
-    assert pack.range_errors() == 0
+    assert dc1.range_errors() == 0 and dc2.range_errors() == 0
 
 
 # ------------------------------------------------------------ the workloads
 
-def _sample_rows(case, n, seed):
-    rng = np.random.default_rng(seed)
-    rows = rng.choice(case.T, size=min(n, case.T), replace=False)
-    return np.unique(np.concatenate([rows, [0, case.T - 1]]))
-
-
-@pytest.mark.parametrize("name,sample", [
-    ("tiny", None), ("decode_commit", None), ("wide_gqa_d64", None), ("biased_fp16", 768),
-    ("prefill_8k", 384), ("decode_commit_kv1", None), ("decode_commit_kv2", None)])
-def test_workload(name, sample):
+@pytest.mark.parametrize("name", ["tiny", "decode_commit", "wide_gqa_d64", "biased_fp16",
+                                  "prefill_8k", "decode_commit_kv1", "decode_commit_kv2"])
+def test_workload(name):
+    """Every stored row of every workload at its full size, element by element."""
     case = W.workload(name)
-    rows = None if sample is None else _sample_rows(case, sample, 5)
-    _, _, st = _run(case, name, rows)
+    dc, pack, st = _run(case, name)
+    say(f"  plan: {pack.plan(case.T, case.commit_lens is not None)}")
     # diagnostic only; the bar is the tolerance above
     assert st["exact_frac"] > 0.9
 
@@ -274,8 +277,7 @@ def test_max_layers(T, row_width):
     the tiled path)."""
     kw = dict(row_width=row_width, commit_range=(0, 8)) if row_width else {}
     case = W.make_case(T=T, H=128, L=dk.MAX_LAYERS, NH=1, D=64, slots=T + 50, seed=34 + T, **kw)
-    rows = None if T < 1000 else _sample_rows(case, 256, 6)
-    _run(case, f"{dk.MAX_LAYERS} layers, T={T}", rows)
+    _run(case, f"{dk.MAX_LAYERS} layers, T={T}")
 
 
 def test_all_rows_skipped_and_empty():
@@ -288,8 +290,8 @@ def test_all_rows_skipped_and_empty():
     # T == 0: OK and nothing enqueued
     empty = torch.empty((0, case.H), dtype=torch.bfloat16, device="cuda")
     e64 = torch.empty((0,), dtype=torch.int64, device="cuda")
-    assert dk.ctx_kv_write(pack, empty, e64, e64, dc.pool_descs())
-    assert pack.range_errors() == 0
+    assert dk.ctx_kv_write(pack, empty, e64, e64, dc.pool_descs(), range_errors=dc.err)
+    assert dc.range_errors() == 0
 
 
 @pytest.mark.parametrize("H", [64, 1024], ids=["plain", "k_split"])
@@ -304,8 +306,8 @@ def test_out_of_range_rows_are_skipped_and_counted(H):
     pack = dc.pack()
     assert dc.write(pack)
     torch.cuda.synchronize()
-    assert pack.range_errors() == 3 * case.L
-    assert pack.range_errors() == 0  # read-and-clear
+    assert dc.range_errors() == 3 * case.L
+    assert dc.range_errors() == 0  # read-and-clear
     skipped = {3, 5, 7}
     want = np.sort([case.locs[t] for t in range(case.T) if t not in skipped])
     assert np.array_equal(np.sort(dc.touched_slots(0, "k")), want)
@@ -333,16 +335,116 @@ def test_pool_layout_fallback_and_invalid_pairing():
     raw = lambda **kw: dk.ctx_kv_write_raw(
         pack, dc.x.data_ptr(), kw.get("T", 8), case.H, dc.positions.data_ptr(),
         dc.locs.data_ptr(), kw.get("commit"), kw.get("W", 0), kw.get("B", 0),
-        kw.get("pools", pools), None)[0]
+        kw.get("pools", pools), None, flags=kw.get("flags", 0))[0]
     assert raw(commit=dc.commit.data_ptr()) == dk.E_INVALID               # commit without W
     assert raw(W=4, B=2) == dk.E_INVALID                                  # W without commit
     assert raw(commit=dc.commit.data_ptr(), W=4, B=3) == dk.E_INVALID     # B*W != T
     assert raw(pools=pools[:1]) == dk.E_INVALID                           # wrong pool count
     assert raw(T=-1) == dk.E_INVALID
+    assert raw(commit=dc.commit.data_ptr(), W=4, B=2, flags=2) == dk.E_INVALID  # unknown flag
     with pytest.raises(ValueError):
         dk.ctx_kv_write(pack, dc.x, dc.positions, dc.locs, pools, commit_lens=dc.commit)
+    # the binding's own checks: index dtypes and lengths, the activation dtype
+    with pytest.raises(ValueError):
+        dk.ctx_kv_write(pack, dc.x, dc.positions.to(torch.int32), dc.locs, pools,
+                        commit_lens=dc.commit, locs_row_width=4)
+    with pytest.raises(ValueError):
+        dk.ctx_kv_write(pack, dc.x, dc.positions, dc.locs[:7], pools, commit_lens=dc.commit,
+                        locs_row_width=4)
+    with pytest.raises(ValueError):
+        dk.ctx_kv_write(pack, dc.x, dc.positions, dc.locs, pools,
+                        commit_lens=dc.commit.to(torch.int32), locs_row_width=4)
+    with pytest.raises(ValueError):
+        dk.ctx_kv_write(pack, dc.x.to(torch.float16), dc.positions, dc.locs, pools,
+                        commit_lens=dc.commit, locs_row_width=4)
+    with pytest.raises(ValueError):
+        dk.ctx_kv_write(pack, dc.x, dc.positions[::2].repeat_interleave(2)[:8].contiguous()
+                        .cpu(), dc.locs, pools, commit_lens=dc.commit, locs_row_width=4)
     torch.cuda.synchronize()
     assert len(dc.touched_slots(0, "k")) == 0
+
+
+def test_k_split_workspace_is_required():
+    """A K-split write without a large enough workspace is E_INVALID and
+    enqueues nothing."""
+    case = W.make_case(T=64, H=1024, L=1, NH=1, D=128, slots=128, seed=47)
+    dc = DeviceCase(case)
+    pack = dc.pack()
+    need = pack.workspace_bytes(case.T, False)
+    assert need > 0 and pack.plan(case.T, False)["kernel"] == "stream_ksplit"
+    small = torch.empty(need - 16, dtype=torch.uint8, device="cuda")
+    raw = lambda ws, n: dk.ctx_kv_write_raw(
+        pack, dc.x.data_ptr(), case.T, case.H, dc.positions.data_ptr(), dc.locs.data_ptr(),
+        None, 0, 0, dc.pool_descs(), None, workspace=ws, workspace_bytes=n)[0]
+    assert raw(None, 0) == dk.E_INVALID
+    assert raw(small.data_ptr(), small.numel()) == dk.E_INVALID
+    torch.cuda.synchronize()
+    assert len(dc.touched_slots(0, "k")) == 0
+
+
+def _validate_case(**kw):
+    return W.make_case(T=24, H=64, L=2, NH=1, D=64, row_width=8, commit_range=(1, 8),
+                       slots=40, P=64, seed=48, **kw)
+
+
+@pytest.mark.parametrize("what", ["position", "slot", "duplicate"])
+def test_validate_mode_reports_range_errors(what):
+    """Validate mode: an out-of-table position, a slot past the pool, or two
+    stored rows naming one slot return E_RANGE with the cause and write
+    nothing."""
+    case = _validate_case()
+    case.commit_lens[:] = 8
+    if what == "position":
+        case.positions[9] = case.P
+        cause = dk.RANGE_POSITION
+    elif what == "slot":
+        case.locs[17] = case.slots
+        cause = dk.RANGE_SLOT
+    else:
+        case.locs[20] = case.locs[2]
+        cause = dk.RANGE_DUPLICATE
+    dc = DeviceCase(case)
+    pack = dc.pack()
+    say(f"[case] validate mode: {what}")
+    with pytest.raises(dk.RangeError) as e:
+        dc.write(pack, validate=True)
+    assert e.value.cause == cause
+    torch.cuda.synchronize()
+    assert len(dc.touched_slots(0, "k")) == 0 and len(dc.touched_slots(1, "v")) == 0
+
+
+def test_validate_mode_ignores_rows_that_are_not_stored():
+    """Rows past a request's commit length or with a negative slot are not
+    checked (they are never stored): a duplicate or bad position there passes,
+    and the write then matches the oracle."""
+    case = _validate_case()
+    case.commit_lens[:] = [3, 8, 5]
+    case.locs[6] = case.locs[0]          # truncated column of request 0
+    case.positions[7] = 10 ** 6          # truncated too
+    case.locs[12] = -1
+    case.positions[12] = -5              # negative slot: skipped
+    dc, pack, _ = _run(case, "validate: unchecked rows")
+    dc.reset_pools()
+    assert dc.write(pack, validate=True)
+    torch.cuda.synchronize()
+    check_slot_sets(dc)
+    compare_rows(dc, None, "validate mode")
+    assert dc.range_errors() == 0
+
+
+def test_fallback_logging(capfd, monkeypatch):
+    """DSPARK_LOG=1 prints the reason of the first write fallback of a pack."""
+    monkeypatch.setenv("DSPARK_LOG", "1")
+    case = W.make_case(T=8, H=64, L=1, NH=1, D=64, slots=16, seed=49)
+    dc = DeviceCase(case)
+    pack = dc.pack()
+    bad = dc.pool_descs()
+    bad[0].k_stride1 = 2 * case.D
+    assert dk.ctx_kv_write(pack, dc.x, dc.positions, dc.locs, bad) is False
+    assert dk.ctx_kv_write(pack, dc.x, dc.positions, dc.locs, bad) is False
+    err = capfd.readouterr().err
+    assert err.count("dspark_ctx_kv_write fell back") == 1
+    assert "pool dtype, layout or alignment" in err or "KV pool dtype" in err
 
 
 def test_rope_tables_by_content():
@@ -366,17 +468,19 @@ def test_graph_replays_match_eager(H):
     """The write captured in a HIP graph (as the benchmark times it) gives the
     eager result on every replay, with eager work and syncs between replays.
     At H = 1024 K is split over workgroups: two launches per write, sharing
-    the pack's workspace across replays."""
+    one caller workspace across replays."""
     case = W.make_case(T=96, H=H, L=2, NH=2, D=128, row_width=8, slots=256, seed=31)
     dc, pack, _ = _run(case, "eager reference")
     k_ref, v_ref = dc.pools_host()
+    ws = dc.workspace(pack)
+    assert (ws is not None) == (H == 1024)
     side = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     dc.reset_pools()
     torch.cuda.synchronize()
     with torch.cuda.stream(side):
         with torch.cuda.graph(g, stream=side):
-            assert dc.write(pack)
+            assert dc.write(pack, workspace=ws)
     for rep in range(4):
         for p in dc.pk + dc.pv:
             p.view(torch.int16).fill_(-1)

@@ -68,13 +68,8 @@ def test_random_shape(i):
     assert dc.write(pack)
     torch.cuda.synchronize()
     check_slot_sets(dc)
-    rows = None
-    if case.T > 1500:
-        rng = np.random.default_rng(i)
-        rows = np.unique(np.concatenate([rng.choice(case.T, 400, replace=False),
-                                         [0, case.T - 1]]))
-    st = compare_rows(dc, rows, f"sweep{i}")
-    assert pack.range_errors() == 0
+    st = compare_rows(dc, None, f"sweep{i}")  # every stored row
+    assert dc.range_errors() == 0
     say(f"  ok: {st}")
     pack.free()
 
@@ -121,7 +116,7 @@ def test_random_shape_k_split(i):
     torch.cuda.synchronize()
     check_slot_sets(dc)
     st = compare_rows(dc, None, f"ksweep{i}")
-    assert pack.range_errors() == 0
+    assert dc.range_errors() == 0
     say(f"  ok: {st}")
     pack.free()
 

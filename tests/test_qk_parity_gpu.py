@@ -122,14 +122,11 @@ def test_small_cases(name):
     _run(c, name)
 
 
-@pytest.mark.parametrize("name,sample", [("qk_decode", None), ("qk_prefill_8k", 512)])
-def test_workloads(name, sample):
+@pytest.mark.parametrize("name", ["qk_decode", "qk_prefill_8k"])
+def test_workloads(name):
+    """Every token of the workload at its full size, element by element."""
     c = W.qk_workload(name)
-    rows = None
-    if sample:
-        rng = np.random.default_rng(7)
-        rows = np.unique(np.concatenate([rng.choice(c.T, sample, replace=False), [0, c.T - 1]]))
-    _, _, exact = _run(c, name, rows)
+    _, _, exact = _run(c, name)
     assert exact > 0.9  # diagnostic only; the bar is the tolerance
 
 
@@ -153,8 +150,8 @@ def test_unsupported_head_dim_falls_back_untouched():
     c = W.make_qk_case(T=4, NHQ=1, NHK=1, D=64, seed=53)
     d = DevQk(c)
     # head_dim 32 over the same buffer: not supported, nothing may change
-    assert not dk.table_qk_norm_rope(d.qkv, d.pos, d.qw[:32], d.kw[:32], d.table[:, :32],
-                                     2, 2, 32, c.eps)
+    assert not dk.table_qk_norm_rope(d.qkv, d.pos, d.qw[:32], d.kw[:32],
+                                     d.table[:, :32].contiguous(), 2, 2, 32, c.eps)
     assert np.array_equal(d.host(), c.qkv)
 
 
