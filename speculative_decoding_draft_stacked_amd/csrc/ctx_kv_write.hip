@@ -20,8 +20,8 @@
 //     workgroup, the weight streamed from HBM into registers;
 //   - the same kernel with K split over workgroups, when few weight tiles
 //     would leave the device idle (e.g. one GPU's share of the KV heads): fp32
-//     part sums to the pack's workspace, then ctx_kv_stream_reduce adds them
-//     in part order and runs the epilogue;
+//     part sums to the caller's workspace, then ctx_kv_stream_reduce adds
+//     them in part order and runs the epilogue;
 //   - ctx_kv_tiled_kernel, large T: 256 rows x 128/192/256 tokens per
 //     workgroup, both operands staged through an LDS ring by direct-to-LDS
 //     loads.
@@ -261,23 +261,28 @@ __device__ __forceinline__ void wait_ring() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));
 }
 
-// LDS-tiled kernel for large T. A workgroup owns a 256-row x 256-token tile
+// LDS-tiled kernel for large T. A workgroup owns a 256-row x BT-token tile
 // (two 128-row weight tiles; the second may lie past the stacked weight when
 // the number of 128-row tiles is odd). Eight waves, two per SIMD, form a 4 x 2
-// grid of 64-row x 128-token wave tiles (2 x 4 MFMA blocks each). The K loop
-// runs over 32-wide sub-chunks (two MFMA steps) through a four-stage LDS ring
-// of 32 KiB stages filled by direct-to-LDS loads three sub-chunks ahead, so
-// the memory pipe never drains between sub-chunks:
-//   - weight: the blocked layout holds, per 64-column chunk, each 32-row group's
-//     A fragment for one MFMA step as one contiguous KiB; a sub-chunk copies
-//     the two steps it needs linearly;
-//   - X: a sub-chunk needs 4 of the 8 16-byte pieces of each token's 64-column
-//     slice (MFMA step s, lane half h takes columns 32h + 8s + [0, 8)); they
-//     sit in a 64-byte LDS row, logical piece p of token t at slot
-//     p ^ ((t / 4) % 4). The LDS serves 16 lanes x 16 bytes per cycle over 64
-//     banks; 16 consecutive tokens then cover all 16 bank groups.
-// The tile is twice as tall as the weight tile so that each K step costs half
-// the line requests per MFMA of a 128-row tile.
+// grid of 64-row x (BT/2)-token wave tiles (2 x BT/64 MFMA blocks each).
+// Operands reach the LDS by direct-to-LDS loads, every load instruction of a
+// wave fetching eight whole 128-byte lines:
+//   - weight: a ring of four 32-wide K sub-chunks (16 KiB each), issued three
+//     sub-chunks ahead; the blocked layout holds, per 64-column chunk, each
+//     32-row group's A fragment for one MFMA step as one contiguous KiB, and a
+//     sub-chunk copies the two steps it needs linearly;
+//   - X: a ring of two 64-wide K chunks (BT x 128 bytes each), issued two
+//     sub-chunks ahead: one token's 64 columns are one line, fetched by eight
+//     consecutive lanes whose 16-byte pieces land at slot s of the token's LDS
+//     row, holding piece s ^ ((t / 2) % 8). A B fragment read (16 lanes, 16
+//     consecutive tokens, one piece) then covers all 64 banks once.
+// The fragments of an MFMA step are read while the MFMAs of the previous step
+// run (software pipeline, one barrier per sub-chunk between the two steps).
+// Wait counts per sub-chunk (loads complete in issue order): with the issue
+// order X(j), W(2j+1) at sub-chunk 2j - 2 and W(2j+2) at 2j - 1, an even
+// sub-chunk finds its X chunk behind at most two weight sub-chunks' loads and
+// an odd one its weight sub-chunk behind one X chunk and two weight
+// sub-chunks.
 template <bool FP16, int D, bool BIAS, bool COMMIT, int BT>
 __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, int t_tiles) {
   using E = Elem<FP16>;
@@ -287,26 +292,25 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
   constexpr int MB = 2;                     // 32-row blocks per wave
   constexpr int NB = BT / 64;               // 32-token blocks per wave
   static_assert(BT % 64 == 0 && BT <= 256, "token tile");
-  constexpr int SK = 32;                    // K per sub-chunk
-  constexpr int STAGES = 4;
-  constexpr int LOOK = STAGES - 1;          // sub-chunks in flight ahead of the MFMAs
+  constexpr int SK = 32;                    // weight K per sub-chunk
+  constexpr int WSTAGES = 4;
+  constexpr int WLOOK = WSTAGES - 1;        // weight sub-chunks in flight ahead
   constexpr int SW = ROWS * SK;             // weight elements per stage
-  // X stage slots: whole rounds of 512 pieces; slots of tokens >= BT read
-  // the zero page so that every thread issues the same loads
-  constexpr int SXE = (BT * SK / 8 + NT - 1) / NT * NT * 8;
-  constexpr int STAGE = SW + SXE;
-  constexpr int W_PER_THREAD = SW / 8 / NT;   // 2 direct loads
-  constexpr int X_PER_THREAD = SXE / 8 / NT;  // 2 direct loads
-  constexpr int LOADS = W_PER_THREAD + X_PER_THREAD;
+  constexpr int SX = BT * BK;               // X elements per stage (one 64-wide chunk)
+  constexpr int W_PER_THREAD = SW / 8 / NT;   // 2 direct loads per sub-chunk
+  constexpr int X_PER_THREAD = SX / 8 / NT;   // BT / 64 direct loads per chunk
+  static_assert(SX == X_PER_THREAD * NT * 8, "X chunk split");
+  constexpr int XOFF = WSTAGES * SW;          // X ring after the weight ring
+  constexpr int RING = XOFF + 2 * SX;
   constexpr int LDO = ROWS + 4;
-  constexpr int SMEM = (STAGES * STAGE > BT * LDO ? STAGES * STAGE : BT * LDO);
+  constexpr int SMEM = (RING > BT * LDO ? RING : BT * LDO);
   __shared__ __align__(16) uint16_t smem[SMEM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wave_n = wave >> 1;  // 64-row group
-  const int wave_t = wave & 1;   // 128-token half
+  const int wave_t = wave & 1;   // token half
   const int r32 = lane & 31;
   const int hh = lane >> 5;
   const int64_t T = a.T;
@@ -342,34 +346,40 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
     const int g = (q % 512) / 128, sp = (q % 128) / 64, l = q % 64;
     wsrc[i] = rt < R ? a.w + rt * nk * 8192 + ((g * 4 + sp) * 64 + l) * 8 : nullptr;
   }
+  // X slot (i * NT + tid) of a chunk: token slot / 8, LDS piece slot % 8,
+  // holding global piece (slot % 8) ^ ((t / 2) % 8) of the token's 64 columns
   int64_t xoff[X_PER_THREAD];
   int xcol[X_PER_THREAD];
 #pragma unroll
   for (int i = 0; i < X_PER_THREAD; ++i) {
     const int slot = i * NT + tid;
-    const int t = slot / 4;
-    const int lp = (slot % 4) ^ ((t >> 2) & 3);   // logical piece held by this slot
-    const int col = 8 * ((lp / 2) * 4 + lp % 2);  // its column in the first half
+    const int t = slot / 8;
+    const int col = 8 * ((slot % 8) ^ ((t >> 1) & 7));
     const int64_t tok = t0 + t < T ? t0 + t : T - 1;  // rows past T are never stored
     xoff[i] = tok * a.x_stride + col;
-    xcol[i] = t < BT ? col : H;  // slots past the tile read the zero page
+    xcol[i] = col;
   }
-  // sub-chunk sc = half sc % 2 of 64-column chunk sc / 2; the second half
-  // takes MFMA steps 2 and 3, i.e. pieces 2, 3, 6, 7
-  auto issue = [&](int sc, int stage) {
-    uint16_t* base = smem + stage * STAGE;
-    const int c = sc >> 1, h = sc & 1;
+  // weight sub-chunk u (half u % 2 of 64-column chunk u / 2) into stage u % 4;
+  // the second half takes MFMA steps 2 and 3
+  auto issue_w = [&](int u) {
+    uint16_t* base = smem + (u % WSTAGES) * SW;
+    const int c = u >> 1, h = u & 1;
     const bool live = c < nk;  // sub-chunks past the end read the zero page
 #pragma unroll
     for (int i = 0; i < W_PER_THREAD; ++i) {
       const uint16_t* src = live && wsrc[i] ? wsrc[i] + (int64_t)c * 8192 + h * 1024 : a.zeros;
       ldg16_to_lds(src, base + (i * NT + wave * 64) * 8);
     }
+  };
+  // X chunk c (64 columns of every token of the tile) into stage c % 2
+  auto issue_x = [&](int c) {
+    uint16_t* base = smem + XOFF + (c & 1) * SX;
+    const bool live = c < nk;
 #pragma unroll
     for (int i = 0; i < X_PER_THREAD; ++i) {
-      const int k = c * BK + 16 * h + xcol[i];
-      const uint16_t* src = live && k < H ? a.x + xoff[i] + c * BK + 16 * h : a.zeros;
-      ldg16_to_lds(src, base + SW + (i * NT + wave * 64) * 8);
+      const int k = c * BK + xcol[i];
+      const uint16_t* src = live && k < H ? a.x + xoff[i] + c * BK : a.zeros;
+      ldg16_to_lds(src, base + (i * NT + wave * 64) * 8);
     }
   };
 
@@ -381,49 +391,82 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
 
-  // Whole turns of the ring with no branches (sub-chunks past the end read
-  // the zero page), so stage indices are compile-time constants and every
-  // wait count is exact.
+  // Software pipeline over MFMA steps: the fragments of a step are read
+  // from the LDS while the MFMAs of the previous step run, so no MFMA waits
+  // on a fragment read issued right before it. Per sub-chunk u:
+  //   read step-1 fragments of u | 8 MFMAs on the step-0 fragments of u
+  //   wait for the loads of u + 1, barrier, issue the next loads
+  //   read step-0 fragments of u + 1 | 8 MFMAs on the step-1 fragments of u
+  // Whole turns of four sub-chunks (two X chunks) with no branches
+  // (sub-chunks past the end read the zero page), so stage indices are
+  // compile-time constants and every wait count is exact.
+  auto read_a = [&](int stage, int sp, vec8(&fa)[MB]) {
+    const uint16_t* ws = smem + stage * SW;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int r = wave_n * 64 + mb * 32;  // first row of the 32-row block
+      const int blk = r / BN;               // which of the two weight blocks
+      const int grp = (r % BN) / 32;        // 32-row group inside the block
+      fa[mb] = *reinterpret_cast<const vec8*>(ws + blk * (BN * SK) +
+                                              ((grp * 2 + sp) * 64 + lane) * 8);
+    }
+  };
+  auto read_b = [&](int u, int sp, vec8(&fb)[NB]) {
+    const uint16_t* xs = smem + XOFF + ((u >> 1) & 1) * SX;
+    const int h = u & 1;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int t = wave_t * (BT / 2) + nb * 32 + r32;
+      // MFMA step s = 2h + sp, lane half hh: columns 32 hh + 8 s + [0, 8)
+      // (the weight's blocked layout pairs the same columns)
+      const int piece = 4 * hh + 2 * h + sp;
+      const int slot = piece ^ ((t >> 1) & 7);
+      fb[nb] = *reinterpret_cast<const vec8*>(xs + (t * 8 + slot) * 8);
+    }
+  };
+  auto mfmas = [&](const vec8(&fa)[MB], const vec8(&fb)[NB]) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = E::mfma(fa[mb], fb[nb], acc[mb][nb]);
+  };
   const int nsub = 2 * nk;
-  const int nsub_ring = (nsub + STAGES - 1) / STAGES * STAGES;
+  const int nsub_ring = (nsub + WSTAGES - 1) / WSTAGES * WSTAGES;
+  vec8 a0[MB], b0[NB], a1[MB], b1[NB];
+  issue_x(0);
 #pragma unroll
-  for (int u = 0; u < LOOK; ++u) issue(u, u);
-  for (int c0 = 0; c0 < nsub_ring; c0 += STAGES) {
+  for (int u = 0; u < WLOOK; ++u) issue_w(u);
+  wait_ring<2 * W_PER_THREAD>();  // X chunk 0 and weight sub-chunk 0
+  raw_barrier();
+  issue_x(1);
+  issue_w(WLOOK);
+  read_a(0, 0, a0);
+  read_b(0, 0, b0);
+  for (int c0 = 0; c0 < nsub_ring; c0 += WSTAGES) {
 #pragma unroll
-    for (int u = 0; u < STAGES; ++u) {
-      wait_ring<(LOOK - 1) * LOADS>();  // this thread's loads of sub-chunk c0 + u landed
-      raw_barrier();                     // ... and everyone's; stage (u - 1) % STAGES is free
-      issue(c0 + u + LOOK, (u + LOOK) % STAGES);
-      const uint16_t* ws = smem + u * STAGE;
-      const uint16_t* xs = ws + SW;
-      vec8 af[2][MB], bfr[2][NB];
-      auto read_frags = [&](int sp, vec8(&fa)[MB], vec8(&fb)[NB]) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const int r = wave_n * 64 + mb * 32;  // first row of the 32-row block
-          const int blk = r / BN;               // which of the two weight blocks
-          const int grp = (r % BN) / 32;        // 32-row group inside the block
-          fa[mb] = *reinterpret_cast<const vec8*>(ws + blk * (BN * SK) +
-                                                  ((grp * 2 + sp) * 64 + lane) * 8);
-        }
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const int t = wave_t * (BT / 2) + nb * 32 + r32;
-          const int slot = (2 * hh + sp) ^ ((t >> 2) & 3);
-          fb[nb] = *reinterpret_cast<const vec8*>(xs + (t * 4 + slot) * 8);
-        }
-      };
-      read_frags(0, af[0], bfr[0]);
-      read_frags(1, af[1], bfr[1]);
-#pragma unroll
-      for (int sp = 0; sp < 2; ++sp)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            acc[mb][nb] = E::mfma(af[sp][mb], bfr[sp][nb], acc[mb][nb]);
+    for (int uu = 0; uu < WSTAGES; ++uu) {
+      const int u = c0 + uu;
+      __builtin_amdgcn_sched_barrier(0);
+      read_a(uu, 1, a1);
+      read_b(uu, 1, b1);
+      mfmas(a0, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      // the loads of sub-chunk u + 1 landed (odd: its X chunk, behind at
+      // most two weight sub-chunks; even: its weight sub-chunk, behind one X
+      // chunk and two weight sub-chunks), this wave's reads of u are done
+      if ((uu + 1) % 2 == 0)
+        wait_ring<2 * W_PER_THREAD>();
+      else
+        wait_ring<2 * W_PER_THREAD + X_PER_THREAD>();
+      raw_barrier();  // ... everyone's: the stages of sub-chunk u are free
+      if ((uu + 1) % 2 == 0) issue_x(((u + 1) >> 1) + 1);
+      issue_w(u + 1 + WLOOK);
+      read_a((uu + 1) % WSTAGES, 0, a0);
+      read_b(u + 1, 0, b0);
+      mfmas(a1, b1);
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
   wait_ring<0>();  // the prefetches past the end (zero page) are done, LDS reads too
   raw_barrier();
 
