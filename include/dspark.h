@@ -44,7 +44,8 @@ enum {
   DSPARK_E_RANGE = -2,     /* validate mode: a stored row's position or slot is out of range,
                               or two stored rows name one slot (see DSPARK_RANGE_*) */
   DSPARK_E_DEVICE = -3,    /* a HIP runtime call failed */
-  DSPARK_E_NOMEM = -4      /* device allocation failed (pack only) */
+  DSPARK_E_NOMEM = -4,     /* device allocation failed (pack only) */
+  DSPARK_E_TOO_LARGE = -5  /* the static scratch cannot hold the workspace needed */
 };
 
 /* Why a pack or a write returned DSPARK_FALLBACK. */
@@ -237,6 +238,30 @@ int dspark_ctx_kv_write(const dspark_ctx_kv_pack* pack, const void* ctx_hidden,
                         int32_t num_pools, void* workspace, int64_t workspace_bytes,
                         unsigned long long* range_errors, uint32_t flags, void* stream,
                         int32_t* detail);
+
+/* The write for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same operation, arguments and kernels as dspark_ctx_kv_write, without the
+ * workspace arguments. Its scratch (the K-split part sums and row map, when
+ * the write splits K) is a file-scope device array of
+ * DSPARK_STATIC_SCRATCH_BYTES bytes, enough for any write on a device of up
+ * to DSPARK_STATIC_SCRATCH_CUS compute units; each device the library runs
+ * on holds its own copy until the process ends. The call allocates nothing,
+ * never synchronises and keeps nothing between calls that must start at
+ * zero. Every call on one device shares that device's scratch: calls that
+ * overlap in time on one device (different streams) race.
+ * flags must be 0 (validate mode synchronises; use dspark_ctx_kv_write).
+ * Returns as dspark_ctx_kv_write, and DSPARK_E_TOO_LARGE when the write
+ * would need more workspace than the scratch holds (nothing enqueued). */
+#define DSPARK_STATIC_SCRATCH_CUS 256
+#define DSPARK_STATIC_SCRATCH_BYTES (256LL * 128 * 128 * 4 + 2048 * 4)
+int dspark_ctx_kv_write_static(const dspark_ctx_kv_pack* pack, const void* ctx_hidden,
+                               int64_t num_tokens, int64_t hidden_row_stride,
+                               const int64_t* positions, const int64_t* locs,
+                               const int64_t* commit_lens, int64_t locs_row_width,
+                               int64_t num_requests, const dspark_pool_desc* pools,
+                               int32_t num_pools, unsigned long long* range_errors,
+                               uint32_t flags, void* stream, int32_t* detail);
 
 /* In-place table QK RMSNorm + neox RoPE on a fused QKV tensor (sglang PR
  * #31847, key source snippets: table_qk_norm_rope_ and

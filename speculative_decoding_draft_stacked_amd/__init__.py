@@ -26,7 +26,7 @@ from typing import Optional, Sequence
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdspark.so")
 
-OK, FALLBACK, E_INVALID, E_RANGE, E_DEVICE, E_NOMEM = 0, 1, -1, -2, -3, -4
+OK, FALLBACK, E_INVALID, E_RANGE, E_DEVICE, E_NOMEM, E_TOO_LARGE = 0, 1, -1, -2, -3, -4, -5
 BF16, FP16, FP32, QUANTIZED = 0, 1, 2, 99
 RANGE_NONE, RANGE_POSITION, RANGE_SLOT, RANGE_DUPLICATE = 0, 1, 2, 3
 WRITE_VALIDATE = 1
@@ -40,7 +40,8 @@ FALLBACK_REASONS = {
 }
 EXPORTS = [
     "dspark_check_eligibility", "dspark_pack_ctx_kv", "dspark_ctx_kv_plan",
-    "dspark_ctx_kv_workspace_bytes", "dspark_ctx_kv_write", "dspark_pack_info",
+    "dspark_ctx_kv_workspace_bytes", "dspark_ctx_kv_write", "dspark_ctx_kv_write_static",
+    "dspark_pack_info",
     "dspark_pack_buffers", "dspark_pack_free", "dspark_status_str", "dspark_fallback_str",
     "dspark_range_str", "dspark_table_qk_norm_rope",
     "dspark_verify_accept", "dspark_pack_main_proj", "dspark_main_proj_workspace_bytes",
@@ -159,6 +160,9 @@ def lib() -> ctypes.CDLL:
         L.dspark_ctx_kv_write.argtypes = [vp, vp, i64, i64, vp, vp, vp, i64, i64,
                                           ctypes.POINTER(PoolDesc), i32, vp, i64, vp,
                                           ctypes.c_uint32, vp, p_i32]
+        L.dspark_ctx_kv_write_static.argtypes = [vp, vp, i64, i64, vp, vp, vp, i64, i64,
+                                                 ctypes.POINTER(PoolDesc), i32, vp,
+                                                 ctypes.c_uint32, vp, p_i32]
         L.dspark_pack_info.argtypes = [vp, p_i32, p_i64, p_i64, p_i64, p_i32, p_i32]
         L.dspark_pack_buffers.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                           ctypes.POINTER(vp)]
@@ -183,6 +187,7 @@ def lib() -> ctypes.CDLL:
         L.dspark_range_str.argtypes = [ctypes.c_int]
         L.dspark_range_str.restype = ctypes.c_char_p
         for name in ("dspark_check_eligibility", "dspark_pack_ctx_kv", "dspark_ctx_kv_write",
+                     "dspark_ctx_kv_write_static",
                      "dspark_ctx_kv_plan", "dspark_ctx_kv_workspace_bytes",
                      "dspark_pack_info", "dspark_pack_buffers",
                      "dspark_table_qk_norm_rope", "dspark_verify_accept",
@@ -438,6 +443,47 @@ def ctx_kv_write(pack: Pack, ctx_hidden, positions, locs, pools: Sequence[PoolDe
     if st == E_RANGE:
         raise RangeError(detail, f"dspark_ctx_kv_write: {range_str(detail)}")
     _raise_for(st, "dspark_ctx_kv_write")
+    return True
+
+
+def ctx_kv_write_static(pack: Pack, ctx_hidden, positions, locs, pools: Sequence[PoolDesc],
+                        commit_lens=None, locs_row_width: Optional[int] = None,
+                        range_errors=None, stream=None) -> bool:
+    """dspark_ctx_kv_write_static: the write with the library's static scratch
+    instead of a caller workspace (allocates nothing). Same checks and
+    results as ctx_kv_write; calls that overlap on one device race."""
+    if (commit_lens is None) != (locs_row_width is None):
+        raise ValueError("commit_lens and locs_row_width must be passed together")
+    info = pack.info()
+    if ctx_hidden.dim() != 2 or ctx_hidden.stride(1) != 1:
+        raise ValueError("ctx_hidden must be [T, hidden] with unit column stride")
+    if str(ctx_hidden.dtype).replace("torch.", "") != _ACT_TORCH.get(info["act_dtype"]):
+        raise ValueError("ctx_hidden is not in the pack's activation dtype")
+    if ctx_hidden.shape[1] != info["hidden"]:
+        raise ValueError(f"ctx_hidden has {ctx_hidden.shape[1]} columns, the pack {info['hidden']}")
+    dev = ctx_hidden.device
+    T = ctx_hidden.shape[0]
+    _check_index("positions", positions, T, dev)
+    _check_index("locs", locs, T, dev)
+    W, B = 0, 0
+    if commit_lens is not None:
+        W = int(locs_row_width)
+        if W <= 0 or T % W:
+            raise ValueError("locs_row_width must be positive and divide the row count")
+        B = T // W
+        _check_index("commit_lens", commit_lens, B, dev)
+    if range_errors is not None:
+        _check_index("range_errors", range_errors, 1, dev)
+    arr = (PoolDesc * max(len(pools), 1))(*pools)
+    detail = ctypes.c_int32(0)
+    st = lib().dspark_ctx_kv_write_static(
+        pack.as_parameter, ctx_hidden.data_ptr(), T, ctx_hidden.stride(0), positions.data_ptr(),
+        locs.data_ptr(), None if commit_lens is None else commit_lens.data_ptr(), W, B, arr,
+        len(pools), None if range_errors is None else range_errors.data_ptr(), 0,
+        _stream(stream), ctypes.byref(detail))
+    if st == FALLBACK:
+        return False
+    _raise_for(st, "dspark_ctx_kv_write_static")
     return True
 
 

@@ -9,10 +9,22 @@
 #include <atomic>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <new>
 #include <vector>
 
 #include "internal.h"
+
+// Scratch of dspark_ctx_kv_write_static: the K-split part sums and row map of
+// one write for up to DSPARK_STATIC_SCRATCH_CUS compute units, in a
+// file-scope device array (each device holds its own copy for the life of the
+// process). Host code uses only the device address that hipGetSymbolAddress
+// returns for it, taken once per device with that device current; the name
+// itself is a host-side stand-in.
+constexpr int64_t kStaticScratchBytes =
+    (int64_t)DSPARK_STATIC_SCRATCH_CUS * 128 * 128 * 4 + dspark::kRowMapInts * 4;
+static_assert(kStaticScratchBytes == DSPARK_STATIC_SCRATCH_BYTES, "header constant");
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 struct dspark_ctx_kv_pack {
   int device;
@@ -305,9 +317,58 @@ int write_impl(const dspark_ctx_kv_pack* p, const void* ctx_hidden, int64_t num_
   return e == hipSuccess ? DSPARK_OK : DSPARK_E_DEVICE;
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device (looked up on the
+// first call on that device).
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DSPARK_E_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+      return DSPARK_E_DEVICE;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSPARK_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int dspark_ctx_kv_write_static(const dspark_ctx_kv_pack* p, const void* ctx_hidden,
+                               int64_t num_tokens, int64_t hidden_row_stride,
+                               const int64_t* positions, const int64_t* locs,
+                               const int64_t* commit_lens, int64_t locs_row_width,
+                               int64_t num_requests, const dspark_pool_desc* pools,
+                               int32_t num_pools, unsigned long long* range_errors,
+                               uint32_t flags, void* stream_ptr, int32_t* detail) {
+  set_reason(detail, DSPARK_FB_NONE);
+  if (!p || num_tokens < 0 || flags != 0) return DSPARK_E_INVALID;
+  void* ws = nullptr;
+  const int64_t need =
+      dspark::plan_workspace_bytes(plan_for(p, num_tokens, commit_lens != nullptr));
+  if (need > kStaticScratchBytes) {
+    if (log_enabled())
+      std::fprintf(stderr,
+                   "dspark: dspark_ctx_kv_write_static: %lld workspace bytes needed, the static "
+                   "scratch holds %lld\n",
+                   (long long)need, (long long)kStaticScratchBytes);
+    return DSPARK_E_TOO_LARGE;
+  }
+  if (need > 0 && num_tokens > 0) {
+    const int st = scratch_on_current_device(&ws);
+    if (st != DSPARK_OK) return st;
+  }
+  return write_impl(p, ctx_hidden, num_tokens, hidden_row_stride, positions, locs, commit_lens,
+                    locs_row_width, num_requests, pools, num_pools, ws,
+                    ws ? kStaticScratchBytes : 0, range_errors, flags, stream_ptr, detail);
+}
 
 int dspark_ctx_kv_write(const dspark_ctx_kv_pack* p, const void* ctx_hidden, int64_t num_tokens,
                         int64_t hidden_row_stride, const int64_t* positions, const int64_t* locs,
@@ -429,6 +490,7 @@ const char* dspark_status_str(int status) {
     case DSPARK_E_RANGE: return "position or slot out of range, or a slot written twice";
     case DSPARK_E_DEVICE: return "HIP runtime error";
     case DSPARK_E_NOMEM: return "device allocation failed";
+    case DSPARK_E_TOO_LARGE: return "workspace needed exceeds the static scratch";
     default: return "unknown status";
   }
 }
