@@ -765,7 +765,9 @@ def run_write(name: str, args, cpu: bool = False, blas: bool = False) -> dict:
 
     dc = DeviceCase(case)
     w_bytes = case.n_tot * case.H * 2
-    copies = max(1, math.ceil(2 * INFINITY_CACHE_BYTES / w_bytes))
+    # enough weight copies to exceed twice the Infinity Cache; a weight too
+    # small to matter (tiny: launch-bound) rotates over at most 64
+    copies = min(max(1, math.ceil(2 * INFINITY_CACHE_BYTES / w_bytes)), 64)
     packs = [dc.pack() for _ in range(copies)]
     pools = dc.pool_descs()
     commit = dc.commit
