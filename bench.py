@@ -65,6 +65,13 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_PROBE_BYTES = 1 << 30
 
 
+def weight_copies(w_bytes: int) -> int:
+    """Rotating copies of a weight of `w_bytes` whose total exceeds twice the
+    Infinity Cache, so each step reads its weight from HBM; a weight too small
+    to matter (launch-bound shapes) rotates over at most 64."""
+    return min(max(1, math.ceil(2 * INFINITY_CACHE_BYTES / w_bytes)), 64)
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -219,7 +226,7 @@ def blas_probe(args) -> int:
     dt = torch.float16 if spec.get("dtype") == W.FP16 else torch.bfloat16
     gen = torch.Generator(device="cuda").manual_seed(7)
     x = torch.randn(T, H, device="cuda", dtype=dt, generator=gen)
-    copies = max(1, math.ceil(2 * INFINITY_CACHE_BYTES / (N * H * 2)))
+    copies = weight_copies(N * H * 2)
     # each weight stored [H, N] contiguous: a plain (non-batched) product with
     # no transposed operand
     wts = [torch.randn(H, N, device="cuda", dtype=dt, generator=gen) for _ in range(copies)]
@@ -366,7 +373,7 @@ def blas_time_us(T: int, N: int, H: int, fp16: bool, steps: int, warmup: int) ->
     dt = torch.float16 if fp16 else torch.bfloat16
     gen = torch.Generator(device="cuda").manual_seed(7)
     x = torch.randn(T, H, device="cuda", dtype=dt, generator=gen)
-    copies = max(1, math.ceil(2 * INFINITY_CACHE_BYTES / (N * H * 2)))
+    copies = weight_copies(N * H * 2)
     wts = [torch.randn(H, N, device="cuda", dtype=dt, generator=gen) for _ in range(copies)]
     out = torch.empty(T, N, device="cuda", dtype=dt)
 
@@ -764,10 +771,7 @@ def run_write(name: str, args, cpu: bool = False, blas: bool = False) -> dict:
     alg = algorithmic(case, written)
 
     dc = DeviceCase(case)
-    w_bytes = case.n_tot * case.H * 2
-    # enough weight copies to exceed twice the Infinity Cache; a weight too
-    # small to matter (tiny: launch-bound) rotates over at most 64
-    copies = min(max(1, math.ceil(2 * INFINITY_CACHE_BYTES / w_bytes)), 64)
+    copies = weight_copies(case.n_tot * case.H * 2)
     packs = [dc.pack() for _ in range(copies)]
     pools = dc.pool_descs()
     commit = dc.commit
