@@ -118,75 +118,121 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
 }
 
 // Epilogue shared by both kernels: from the dtype-rounded LDS tile [BT][LDO]
-// (tokens x the tile's 128 weight rows), normalise + rotate each K head, copy
+// (tokens x the tile's ROWS weight rows), normalise + rotate each K head, copy
 // each V head, and scatter both into the token's slot of the head's layer pool.
 // Each (token, head) is handled by D/16 lanes; lane j owns elements
 // [8j, 8j+8) of the first half and their rotation partners 8j + D/2 + [0, 8).
+// A thread keeps one head and lane slot and walks tokens TSTEP apart. Every
+// global load it needs (slots, commit lengths, positions, norm weight, table
+// rows) is issued before its first pool store: vmcnt counts loads and stores
+// in issue order, so a load issued after a store could not be waited for
+// without also waiting for that store to complete.
 // With a row map (rmap != nullptr), tile token tt is row rmap[tt] (< 0: none).
 template <typename E, int D, int BT, bool COMMIT, int LDO, int NT = NTHREADS, int ROWS = BN>
 __device__ __forceinline__ void scatter_tile(const WriteArgs& a, const uint16_t* sO, int64_t n0,
                                              int64_t t0, int tid, const int* rmap = nullptr) {
-  const int64_t T = a.T;
   constexpr int TPH = D / 16;    // lanes per (token, head)
   constexpr int HPT = ROWS / D;  // heads per tile
   constexpr int TASK_LANES = BT * HPT * TPH;
-  static_assert(NT % 64 == 0 && TASK_LANES % TPH == 0, "lane groups stay inside a wave");
+  static_assert(NT % 64 == 0 && (NT / TPH) % HPT == 0, "a thread keeps one head and lane slot");
+  constexpr int ITERS = (TASK_LANES + NT - 1) / NT;
+  constexpr int TSTEP = NT / TPH / HPT;  // tile tokens between a thread's iterations
+  const int j = tid % TPH;
+  const int hd = (tid / TPH) % HPT;
+  const int tt0 = tid / TPH / HPT;
   const int two_nh = 2 * a.NH;
-#pragma unroll 1
-  for (int idx = tid; idx < TASK_LANES; idx += NT) {
-    const int task = idx / TPH;
-    const int j = idx % TPH;
-    const int tt = task / HPT;
-    const int hd = task % HPT;
+  const int64_t g = (n0 + hd * D) / D;  // global head: layer-major, K heads then V heads
+  if (g >= (int64_t)a.L * two_nh) return;  // rows past the stacked weight (last tile)
+  const int layer = (int)(g / two_nh);
+  const int jj = (int)(g % two_nh);
+  const bool is_k = jj < a.NH;
+  const int n = is_k ? jj : jj - a.NH;
+  const int64_t T = a.T;
+  // the layer's pool and row stride, read once: a kernel-argument array with
+  // a run-time index is read by a vector load, which must not follow a store
+  const int64_t nslots = a.slots[layer];
+  uint16_t* const pool = (is_k ? a.pk[layer] : a.pv[layer]) + n * D + j * 8;
+  const int64_t rstride = is_k ? a.ks0[layer] : a.vs0[layer];
+
+  // indices of every row this thread stores
+  int64_t loc[ITERS], pos[ITERS];
+  int tts[ITERS];
+#pragma unroll
+  for (int k = 0; k < ITERS; ++k) {
+    const int tt = tt0 + k * TSTEP;
+    tts[k] = tt;
+    loc[k] = -1;
+    pos[k] = 0;
+    if (tid + k * NT >= TASK_LANES) continue;  // ragged last pass (uniform per lane group)
     const int64_t t = rmap ? (int64_t)rmap[tt] : t0 + tt;
-    if (t < 0 || t >= T) continue;  // uniform over the TPH lanes of a task
-    const int64_t loc = a.locs[t];
-    bool valid = loc >= 0;
-    if (COMMIT) valid = valid && (t % a.W) < a.commit[t / a.W];
-    if (!valid) continue;
-    const int64_t g = (n0 + hd * D) / D;  // global head: layer-major, K heads then V heads
-    if (g >= (int64_t)a.L * two_nh) continue;  // rows past the stacked weight (last tile)
-    const int layer = (int)(g / two_nh);
-    const int jj = (int)(g % two_nh);
-    const bool is_k = jj < a.NH;
-    const int n = is_k ? jj : jj - a.NH;
-    const int64_t p = a.pos[t];
-    if (p < 0 || p >= a.P || loc >= a.slots[layer]) {
-      if (j == 0 && jj == 0 && a.err) atomicAdd(a.err, 1ull);  // once per (row, layer)
-      continue;
+    if (t < 0 || t >= T) continue;
+    int64_t l = a.locs[t];
+    if (COMMIT && (t % a.W) >= a.commit[t / a.W]) l = -1;
+    loc[k] = l;
+    pos[k] = a.pos[t];
+  }
+  // rows stored: valid (slot >= 0, inside the commit window) and in range
+  bool ok[ITERS];
+#pragma unroll
+  for (int k = 0; k < ITERS; ++k)
+    ok[k] = loc[k] >= 0 && pos[k] >= 0 && pos[k] < a.P && loc[k] < nslots;
+
+  if (is_k) {
+    float gw1[8], gw2[8];
+    const float* gwp = a.knw + (int64_t)layer * D + j * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      gw1[i] = gwp[i];
+      gw2[i] = gwp[i + D / 2];
     }
-    const uint16_t* src = sO + tt * LDO + hd * D + j * 8;
-    const uint4 u1 = *reinterpret_cast<const uint4*>(src);
-    const uint4 u2 = *reinterpret_cast<const uint4*>(src + D / 2);
-    if (is_k) {
+    // table rows (row 0 for rows not stored: always inside the table)
+    float cc[ITERS][8], ss[ITERS][8];
+#pragma unroll
+    for (int k = 0; k < ITERS; ++k) {
+      const float* cs = a.table + (ok[k] ? pos[k] : 0) * D + j * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        cc[k][i] = cs[i];
+        ss[k][i] = cs[i + D / 2];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < ITERS; ++k) {
+      if (loc[k] >= 0 && !ok[k] && j == 0 && jj == 0 && a.err)
+        atomicAdd(a.err, 1ull);  // once per (row, layer)
+      if (!ok[k]) continue;  // uniform over the TPH lanes of a row
+      const uint16_t* src = sO + tts[k] * LDO + hd * D + j * 8;
+      const uint4 u1 = *reinterpret_cast<const uint4*>(src);
+      const uint4 u2 = *reinterpret_cast<const uint4*>(src + D / 2);
       float x1[8], x2[8];
       unpack8<E>(u1, x1);
       unpack8<E>(u2, x2);
-      float ss = 0.0f;
+      float sq = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ss += x1[i] * x1[i] + x2[i] * x2[i];
+      for (int i = 0; i < 8; ++i) sq += x1[i] * x1[i] + x2[i] * x2[i];
 #pragma unroll
-      for (int m = 1; m < TPH; m <<= 1) ss += __shfl_xor(ss, m);
-      const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
-      const float* gw = a.knw + (int64_t)layer * D + j * 8;
-      const float* cs = a.table + p * D + j * 8;
+      for (int m = 1; m < TPH; m <<= 1) sq += __shfl_xor(sq, m);
+      const float inv = 1.0f / sqrtf(sq / (float)D + a.eps);
       float o1[8], o2[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float n1 = E::to_f(E::from_f(x1[i] * inv * gw[i]));
-        const float n2 = E::to_f(E::from_f(x2[i] * inv * gw[i + D / 2]));
-        const float c = cs[i];
-        const float s = cs[i + D / 2];
-        o1[i] = n1 * c - n2 * s;
-        o2[i] = n2 * c + n1 * s;
+        const float n1 = E::to_f(E::from_f(x1[i] * inv * gw1[i]));
+        const float n2 = E::to_f(E::from_f(x2[i] * inv * gw2[i]));
+        o1[i] = n1 * cc[k][i] - n2 * ss[k][i];
+        o2[i] = n2 * cc[k][i] + n1 * ss[k][i];
       }
-      uint16_t* dst = a.pk[layer] + loc * a.ks0[layer] + n * D + j * 8;
+      uint16_t* dst = pool + loc[k] * rstride;
       *reinterpret_cast<uint4*>(dst) = pack8<E>(o1);
       *reinterpret_cast<uint4*>(dst + D / 2) = pack8<E>(o2);
-    } else {
-      uint16_t* dst = a.pv[layer] + loc * a.vs0[layer] + n * D + j * 8;
-      *reinterpret_cast<uint4*>(dst) = u1;
-      *reinterpret_cast<uint4*>(dst + D / 2) = u2;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < ITERS; ++k) {
+      if (!ok[k]) continue;
+      const uint16_t* src = sO + tts[k] * LDO + hd * D + j * 8;
+      uint16_t* dst = pool + loc[k] * rstride;
+      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+      *reinterpret_cast<uint4*>(dst + D / 2) = *reinterpret_cast<const uint4*>(src + D / 2);
     }
   }
 }
