@@ -120,41 +120,60 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
 // Epilogue shared by both kernels: from the dtype-rounded LDS tile [BT][LDO]
 // (tokens x the tile's ROWS weight rows), normalise + rotate each K head, copy
 // each V head, and scatter both into the token's slot of the head's layer pool.
-// Each (token, head) is handled by D/16 lanes; lane j owns elements
-// [8j, 8j+8) of the first half and their rotation partners 8j + D/2 + [0, 8).
-// A thread keeps one head and lane slot and walks tokens TSTEP apart. Every
-// global load it needs (slots, commit lengths, positions, norm weight, table
-// rows) is issued before its first pool store: vmcnt counts loads and stores
-// in issue order, so a load issued after a store could not be waited for
-// without also waiting for that store to complete.
+// D/16 lanes handle a (token, head), lane j owning elements [8j, 8j+8) of the
+// first half and their rotation partners 8j + D/2 + [0, 8). The tile's heads
+// are split into HS groups, HS as small as keeps every thread busy: a thread
+// walks tokens TSTEP apart, each over the heads of its group, so where tokens
+// are plentiful (the tiled kernel) a token's slot, position and table row are
+// loaded once for all of its heads. Every global load a thread needs is issued
+// before its first pool store: vmcnt counts loads and stores in issue order,
+// so a load issued after a store could not be waited for without also waiting
+// for that store to complete.
 // With a row map (rmap != nullptr), tile token tt is row rmap[tt] (< 0: none).
 template <typename E, int D, int BT, bool COMMIT, int LDO, int NT = NTHREADS, int ROWS = BN>
 __device__ __forceinline__ void scatter_tile(const WriteArgs& a, const uint16_t* sO, int64_t n0,
                                              int64_t t0, int tid, const int* rmap = nullptr) {
   constexpr int TPH = D / 16;    // lanes per (token, head)
   constexpr int HPT = ROWS / D;  // heads per tile
-  constexpr int TASK_LANES = BT * HPT * TPH;
-  static_assert(NT % 64 == 0 && (NT / TPH) % HPT == 0, "a thread keeps one head and lane slot");
+  constexpr int HS_FILL = (NT + BT * TPH - 1) / (BT * TPH);
+  constexpr int HS = HPT < HS_FILL ? HPT : HS_FILL;  // head groups
+  constexpr int HPG = HPT / HS;                      // heads per group
+  static_assert(HPT % HS == 0 && NT % 64 == 0 && (NT / TPH) % HS == 0,
+                "a thread keeps one lane slot and head group");
+  constexpr int TASK_LANES = BT * HS * TPH;
   constexpr int ITERS = (TASK_LANES + NT - 1) / NT;
-  constexpr int TSTEP = NT / TPH / HPT;  // tile tokens between a thread's iterations
+  constexpr int TSTEP = NT / TPH / HS;  // tile tokens between a thread's iterations
   const int j = tid % TPH;
-  const int hd = (tid / TPH) % HPT;
-  const int tt0 = tid / TPH / HPT;
+  const int hs = (tid / TPH) % HS;
+  const int tt0 = tid / TPH / HS;
   const int two_nh = 2 * a.NH;
-  const int64_t g = (n0 + hd * D) / D;  // global head: layer-major, K heads then V heads
-  if (g >= (int64_t)a.L * two_nh) return;  // rows past the stacked weight (last tile)
-  const int layer = (int)(g / two_nh);
-  const int jj = (int)(g % two_nh);
-  const bool is_k = jj < a.NH;
-  const int n = is_k ? jj : jj - a.NH;
   const int64_t T = a.T;
-  // the layer's pool and row stride, read once: a kernel-argument array with
-  // a run-time index is read by a vector load, which must not follow a store
-  const int64_t nslots = a.slots[layer];
-  uint16_t* const pool = (is_k ? a.pk[layer] : a.pv[layer]) + n * D + j * 8;
-  const int64_t rstride = is_k ? a.ks0[layer] : a.vs0[layer];
 
-  // indices of every row this thread stores
+  // the group's heads: pool, row stride and size of the head's layer, read
+  // once (a kernel-argument array with a run-time index is read by a vector
+  // load, which must not follow a store)
+  bool live[HPG], is_k[HPG], counts[HPG];
+  uint16_t* pool[HPG];
+  int64_t rstride[HPG], nslots[HPG];
+  int hlayer[HPG];
+  bool any_k = false;
+#pragma unroll
+  for (int h = 0; h < HPG; ++h) {
+    const int64_t g = (n0 + (hs * HPG + h) * D) / D;  // global head: layer-major, K then V
+    live[h] = g < (int64_t)a.L * two_nh;  // false: rows past the stacked weight (last tile)
+    const int layer = live[h] ? (int)(g / two_nh) : 0;
+    const int jj = (int)(g % two_nh);
+    is_k[h] = live[h] && jj < a.NH;
+    counts[h] = live[h] && jj == 0;  // the layer's first K head counts range errors
+    any_k = any_k || is_k[h];
+    hlayer[h] = layer;
+    const int n = jj < a.NH ? jj : jj - a.NH;
+    pool[h] = (is_k[h] ? a.pk[layer] : a.pv[layer]) + n * D + j * 8;
+    rstride[h] = is_k[h] ? a.ks0[layer] : a.vs0[layer];
+    nslots[h] = a.slots[layer];
+  }
+
+  // indices of every token this thread stores
   int64_t loc[ITERS], pos[ITERS];
   int tts[ITERS];
 #pragma unroll
@@ -171,68 +190,73 @@ __device__ __forceinline__ void scatter_tile(const WriteArgs& a, const uint16_t*
     loc[k] = l;
     pos[k] = a.pos[t];
   }
-  // rows stored: valid (slot >= 0, inside the commit window) and in range
-  bool ok[ITERS];
+  bool pos_ok[ITERS];
 #pragma unroll
-  for (int k = 0; k < ITERS; ++k)
-    ok[k] = loc[k] >= 0 && pos[k] >= 0 && pos[k] < a.P && loc[k] < nslots;
+  for (int k = 0; k < ITERS; ++k) pos_ok[k] = loc[k] >= 0 && pos[k] >= 0 && pos[k] < a.P;
 
-  if (is_k) {
-    float gw1[8], gw2[8];
-    const float* gwp = a.knw + (int64_t)layer * D + j * 8;
+  // K heads: norm weights of their layers and the tokens' table rows (row 0
+  // for tokens not stored: always inside the table)
+  float gw1[HPG][8], gw2[HPG][8];
+  float cc[ITERS][8], ss[ITERS][8];
+  if (any_k) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      gw1[i] = gwp[i];
-      gw2[i] = gwp[i + D / 2];
+    for (int h = 0; h < HPG; ++h) {
+      const float* gwp = a.knw + (int64_t)hlayer[h] * D + j * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        gw1[h][i] = gwp[i];
+        gw2[h][i] = gwp[i + D / 2];
+      }
     }
-    // table rows (row 0 for rows not stored: always inside the table)
-    float cc[ITERS][8], ss[ITERS][8];
 #pragma unroll
     for (int k = 0; k < ITERS; ++k) {
-      const float* cs = a.table + (ok[k] ? pos[k] : 0) * D + j * 8;
+      const float* cs = a.table + (pos_ok[k] ? pos[k] : 0) * D + j * 8;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         cc[k][i] = cs[i];
         ss[k][i] = cs[i + D / 2];
       }
     }
+  }
+
 #pragma unroll
-    for (int k = 0; k < ITERS; ++k) {
-      if (loc[k] >= 0 && !ok[k] && j == 0 && jj == 0 && a.err)
-        atomicAdd(a.err, 1ull);  // once per (row, layer)
-      if (!ok[k]) continue;  // uniform over the TPH lanes of a row
-      const uint16_t* src = sO + tts[k] * LDO + hd * D + j * 8;
+  for (int k = 0; k < ITERS; ++k) {
+    if (loc[k] < 0) continue;  // not stored (uniform over the TPH lanes of a token)
+#pragma unroll
+    for (int h = 0; h < HPG; ++h) {
+      if (!live[h]) continue;
+      if (!pos_ok[k] || loc[k] >= nslots[h]) {
+        if (counts[h] && j == 0 && a.err) atomicAdd(a.err, 1ull);  // once per (row, layer)
+        continue;
+      }
+      const uint16_t* src = sO + tts[k] * LDO + (hs * HPG + h) * D + j * 8;
       const uint4 u1 = *reinterpret_cast<const uint4*>(src);
       const uint4 u2 = *reinterpret_cast<const uint4*>(src + D / 2);
-      float x1[8], x2[8];
-      unpack8<E>(u1, x1);
-      unpack8<E>(u2, x2);
-      float sq = 0.0f;
+      uint16_t* dst = pool[h] + loc[k] * rstride[h];
+      if (is_k[h]) {
+        float x1[8], x2[8];
+        unpack8<E>(u1, x1);
+        unpack8<E>(u2, x2);
+        float sq = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sq += x1[i] * x1[i] + x2[i] * x2[i];
+        for (int i = 0; i < 8; ++i) sq += x1[i] * x1[i] + x2[i] * x2[i];
 #pragma unroll
-      for (int m = 1; m < TPH; m <<= 1) sq += __shfl_xor(sq, m);
-      const float inv = 1.0f / sqrtf(sq / (float)D + a.eps);
-      float o1[8], o2[8];
+        for (int m = 1; m < TPH; m <<= 1) sq += __shfl_xor(sq, m);
+        const float inv = 1.0f / sqrtf(sq / (float)D + a.eps);
+        float o1[8], o2[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float n1 = E::to_f(E::from_f(x1[i] * inv * gw1[i]));
-        const float n2 = E::to_f(E::from_f(x2[i] * inv * gw2[i]));
-        o1[i] = n1 * cc[k][i] - n2 * ss[k][i];
-        o2[i] = n2 * cc[k][i] + n1 * ss[k][i];
+        for (int i = 0; i < 8; ++i) {
+          const float n1 = E::to_f(E::from_f(x1[i] * inv * gw1[h][i]));
+          const float n2 = E::to_f(E::from_f(x2[i] * inv * gw2[h][i]));
+          o1[i] = n1 * cc[k][i] - n2 * ss[k][i];
+          o2[i] = n2 * cc[k][i] + n1 * ss[k][i];
+        }
+        *reinterpret_cast<uint4*>(dst) = pack8<E>(o1);
+        *reinterpret_cast<uint4*>(dst + D / 2) = pack8<E>(o2);
+      } else {
+        *reinterpret_cast<uint4*>(dst) = u1;
+        *reinterpret_cast<uint4*>(dst + D / 2) = u2;
       }
-      uint16_t* dst = pool + loc[k] * rstride;
-      *reinterpret_cast<uint4*>(dst) = pack8<E>(o1);
-      *reinterpret_cast<uint4*>(dst + D / 2) = pack8<E>(o2);
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < ITERS; ++k) {
-      if (!ok[k]) continue;
-      const uint16_t* src = sO + tts[k] * LDO + hd * D + j * 8;
-      uint16_t* dst = pool + loc[k] * rstride;
-      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
-      *reinterpret_cast<uint4*>(dst + D / 2) = *reinterpret_cast<const uint4*>(src + D / 2);
     }
   }
 }
@@ -350,7 +374,8 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
   constexpr int RING = XOFF + 2 * SX;
   constexpr int LDO = ROWS + 4;
   constexpr int SMEM = (RING > BT * LDO ? RING : BT * LDO);
-  __shared__ __align__(16) uint16_t smem[SMEM];
+  // + the tile's bias rows, past both the ring and the output tile
+  __shared__ __align__(16) uint16_t smem[SMEM + (BIAS ? ROWS : 0)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -479,6 +504,13 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
   const int nsub = 2 * nk;
   const int nsub_ring = (nsub + WSTAGES - 1) / WSTAGES * WSTAGES;
   vec8 a0[MB], b0[NB], a1[MB], b1[NB];
+  // the tile's bias rows, loaded once by 32 threads and kept in registers
+  // until the epilogue (a load older than every ring load: the ring's first
+  // wait covers it)
+  const int64_t n_tot = R * BN;
+  uint4 bias8 = make_uint4(0, 0, 0, 0);
+  if (BIAS && tid < ROWS / 8 && n0 + tid * 8 < n_tot)
+    bias8 = *reinterpret_cast<const uint4*>(a.bias + n0 + tid * 8);
   issue_x(0);
 #pragma unroll
   for (int u = 0; u < WLOOK; ++u) issue_w(u);
@@ -514,10 +546,11 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
   }
   __builtin_amdgcn_sched_barrier(0);
   wait_ring<0>();  // the prefetches past the end (zero page) are done, LDS reads too
+  uint16_t* const sbias = smem + SMEM;
+  if (BIAS && tid < ROWS / 8) *reinterpret_cast<uint4*>(sbias + tid * 8) = bias8;
   raw_barrier();
 
   // accumulators (+ bias) -> dtype, into the LDS tile [BT][LDO]
-  const int64_t n_tot = R * BN;
   uint16_t* sO = smem;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -531,7 +564,7 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           v[i] = acc[mb][nb][4 * q + i];
-          if (BIAS && n0 + row + i < n_tot) v[i] += E::to_f(a.bias[n0 + row + i]);
+          if (BIAS) v[i] += E::to_f(sbias[row + i]);  // zero past the stacked weight
         }
         uint2 packed;
         packed.x = E::from_f(v[0]) | (E::from_f(v[1]) << 16);
