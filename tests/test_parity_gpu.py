@@ -84,6 +84,11 @@ SMALL = {
     # 256-token tiles (tail of 178), K tail 8, commit window 10 with holes
     "tiled_t256_commit": dict(T=25010, H=136, L=2, NH=1, D=128, row_width=10,
                               commit_range=(0, 12), neg_loc_frac=0.05, slots=25100),
+    # 128-token tiles, fp16 + stacked bias, an odd number of 128-row weight
+    # tiles (the last workgroup tile's bias rows past the stacked weight read
+    # as zero), four 64-wide heads per workgroup tile spanning two layers
+    "tiled_d64_bias_odd_tiles": dict(T=11000, H=200, L=3, NH=1, D=64, dtype="fp16",
+                                     bias=True, slots=11500),
 }
 
 
@@ -294,16 +299,21 @@ def test_all_rows_skipped_and_empty():
     assert dc.range_errors() == 0
 
 
-@pytest.mark.parametrize("H", [64, 1024], ids=["plain", "k_split"])
-def test_out_of_range_rows_are_skipped_and_counted(H):
+@pytest.mark.parametrize("T,H,L,NH,slots", [(20, 64, 2, 1, 32), (20, 1024, 2, 1, 32),
+                                              (6000, 64, 3, 2, 6050)],
+                         ids=["plain", "k_split", "tiled"])
+def test_out_of_range_rows_are_skipped_and_counted(T, H, L, NH, slots):
     # H = 1024: two weight tiles and 16 chunks of 64, so K is split over
-    # workgroups and the count comes from the reduce launch
-    case = W.make_case(T=20, H=H, L=2, NH=1, D=64, slots=32, P=64, seed=28)
+    # workgroups and the count comes from the reduce launch; T = 6000 over six
+    # weight tiles takes the tiled kernel
+    case = W.make_case(T=T, H=H, L=L, NH=NH, D=64, slots=slots, P=64, seed=28)
     case.positions[3] = 64       # == P
     case.positions[5] = -2
-    case.locs[7] = 32            # == slots
+    case.locs[7] = slots         # == slots
     dc = DeviceCase(case)
     pack = dc.pack()
+    want_kernel = {20: "stream_ksplit" if H == 1024 else "stream", 6000: "tiled"}[T]
+    assert pack.plan(T, False)["kernel"] == want_kernel
     assert dc.write(pack)
     torch.cuda.synchronize()
     assert dc.range_errors() == 3 * case.L
