@@ -8,8 +8,11 @@ Each case draws T, H, L, KV heads, head_dim, dtype, bias, and the slot map
 seed, so the sweep crosses both kernels, their tile and token-split choices,
 K tails, commit-window compaction and its limit. A second sweep draws shapes
 with few weight tiles, H >= 1024 and T <= 1024, which take the K-split form
-(K parts over workgroups, parts added in a second launch). Sizes keep the
-fp64 oracle to about a second per case.
+(K parts over workgroups, parts added in a second launch). A third draws
+shapes for the LDS-tiled kernel: T large enough for its plan, D = 64 tiles
+holding four heads that may span two layers, odd weight-tile counts whose
+last workgroup tile lies half past the stacked weight, bias, commit windows
+and negative slots. Sizes keep the fp64 oracle to about a second per case.
 """
 
 import numpy as np
@@ -120,3 +123,66 @@ def test_random_shape_k_split(i):
     say(f"  ok: {st}")
     pack.free()
 
+
+# ------------------------------------------------ shapes for the tiled kernel
+
+N_TILED_CASES = 10
+
+
+def _draw_tiled(i):
+    """Few heads and a narrow hidden size so that a T past the tiled kernel's
+    threshold keeps the oracle cheap."""
+    rng = np.random.default_rng(9700 + i)
+    D = int(rng.choice([64, 128]))
+    NH = int(rng.integers(1, 4))
+    L = int(rng.integers(1, 5))
+    H = int(rng.integers(8, 41)) * 8
+    dtype = "fp16" if rng.random() < 0.4 else "bf16"
+    bias = bool(rng.random() < 0.5)
+    kw = dict(name=f"tsweep{i}", H=H, L=L, NH=NH, D=D, dtype=dtype, bias=bias,
+              seed=9700 + i, theta=float(rng.choice([1e4, 5e4, 1e6])), P=4096,
+              neg_loc_frac=float(rng.choice([0.0, 0.05])))
+    if rng.random() < 0.4:
+        Wd = int(rng.integers(2, 17))
+        kw.update(row_width=Wd, commit_range=(0, Wd + 2))
+    return kw, int(rng.integers(1, 3000))
+
+
+@pytest.mark.parametrize("i", range(N_TILED_CASES))
+def test_random_shape_tiled(i):
+    kw, extra = _draw_tiled(i)
+    # the smallest T the device's plan gives to the tiled kernel, plus a
+    # ragged amount
+    probe = W.make_case(T=64, slots=64, **{k: v for k, v in kw.items()
+                                          if k not in ("row_width", "commit_range")})
+    pdc = DeviceCase(probe)
+    ppack = pdc.pack()
+    T = 64
+    while ppack.plan(T, False)["kernel"] != "tiled":
+        T *= 2
+    lo = T // 2
+    while lo + 1 < T:  # bisect the threshold
+        mid = (lo + T) // 2
+        if ppack.plan(mid, False)["kernel"] == "tiled":
+            T = mid
+        else:
+            lo = mid
+    ppack.free()
+    del pdc
+    T += extra
+    if "row_width" in kw:
+        T = T // kw["row_width"] * kw["row_width"]
+    case = W.make_case(T=T, slots=T + 37, **kw)
+    say(f"[tsweep {i}] T={case.T} H={case.H} L={case.L} NH={case.NH} D={case.D} {case.dtype} "
+        f"bias={case.qkv_b is not None} W={case.row_width}")
+    dc = DeviceCase(case)
+    pack = dc.pack()
+    plan = pack.plan(case.T, case.commit_lens is not None)
+    assert plan["kernel"] == "tiled", plan
+    assert dc.write(pack)
+    torch.cuda.synchronize()
+    check_slot_sets(dc)
+    st = compare_rows(dc, None, f"tsweep{i}")
+    assert dc.range_errors() == 0
+    say(f"  ok: {plan['token_tile']}-token tiles, {st}")
+    pack.free()
