@@ -89,6 +89,13 @@ SMALL = {
     # as zero), four 64-wide heads per workgroup tile spanning two layers
     "tiled_d64_bias_odd_tiles": dict(T=11000, H=200, L=3, NH=1, D=64, dtype="fp16",
                                      bias=True, slots=11500),
+    # the narrowest hidden size: one K chunk of which 56 of 64 columns are tail
+    "hidden_8_stream": dict(T=40, H=8, L=2, NH=1, D=128, slots=64),
+    "hidden_8_tiled": dict(T=20000, H=8, L=2, NH=1, D=64, dtype="fp16", bias=True,
+                           slots=20100),
+    # one request, one column: commit window of width 1 (lengths 0..3)
+    "window_width_1": dict(T=1, H=64, L=2, NH=2, D=64, row_width=1, commit_range=(0, 3),
+                           slots=8),
 }
 
 
