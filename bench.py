@@ -22,10 +22,10 @@ and attn_decode_8k and attn_d64_16k the draft attention (dspark_draft_attention)
 Timing: W warmup steps, then exactly K steps, each bracketed by a device
 synchronisation. The steps are captured into a HIP graph first, so host launch
 overhead (a ctypes call per step) does not pace the device; every step still
-runs the full write. Write workloads replay the K-step graph once, untimed,
-before the timed replay (the first replay of a heavy workload runs at a lower
-clock; its time is reported as first_replay_us), and 15 more times after it
-for the median and p10/p90. Successive steps use different packed copies of the
+runs the full write. Write workloads replay the K-step graph, untimed, for
+at least 50 ms of device time before the timed replay (the clock ramps up
+under sustained load; the first replay's time is reported as
+first_replay_us), and 15 more times after it for the median and p10/p90. Successive steps use different packed copies of the
 stacked weight, enough copies to exceed the 256 MB Infinity Cache, so each
 step streams its weights from HBM as it would after a target-model forward.
 """
@@ -49,6 +49,9 @@ HEADLINE = "prefill_8k"
 WRITE_CONFIGS = ["tiny", "decode_commit", "prefill_8k", "biased_fp16", "wide_gqa_d64",
                  "decode_commit_kv1", "decode_commit_kv2"]
 SPREAD_REPLAYS = 15  # extra graph replays after the timed one, for median / p10 / p90
+SETTLE_MS = 50.0     # untimed graph replays before the timed one: at least this much device
+                     # time (the clock ramps up over the first ~30 ms of sustained load)
+SETTLE_MAX_REPLAYS = 200
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
 INFINITY_CACHE_BYTES = 256 << 20
@@ -243,10 +246,16 @@ def blas_probe(args) -> int:
     return 0
 
 
+def blas_cores() -> tuple:
+    """(threads the BLAS library runs, CPUs in the process's affinity mask)."""
+    from threadpoolctl import threadpool_info
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return int(threads), len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(case, seconds: float) -> dict:
     """The CPU oracle on the same batch, repeated for about `seconds`."""
     import numpy as np
-    from threadpoolctl import threadpool_info
 
     from oracle import ctx_kv_oracle as O
     from speculative_decoding_draft_stacked_amd import workloads as W
@@ -259,10 +268,9 @@ def cpu_baseline(case, seconds: float) -> dict:
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    affinity = len(os.sched_getaffinity(0))
+    threads, affinity = blas_cores()
     del ks, vs, np
-    return {"value": case.T * reps / el, "unit": "rows/s", "cores": int(min(threads, affinity)),
+    return {"value": case.T * reps / el, "unit": "rows/s", "cores": min(threads, affinity),
             "kind": "oracle",
             "sample": f"{reps} full passes of the {case.name} batch ({case.T} rows, {case.L} "
                       f"layers) in {el:.1f} s; numpy fp64 with BLAS dgemm for the projection "
@@ -272,8 +280,6 @@ def cpu_baseline(case, seconds: float) -> dict:
 
 def qk_cpu_baseline(c, seconds: float) -> dict:
     """The QK oracle on the same batch, repeated for about `seconds`."""
-    from threadpoolctl import threadpool_info
-
     from oracle import qk_norm_rope_oracle as Q
 
     reps, t0 = 0, time.perf_counter()
@@ -285,23 +291,25 @@ def qk_cpu_baseline(c, seconds: float) -> dict:
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": c.T * reps / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": c.T * reps / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{reps} full passes of the {c.name} batch ({c.T} tokens, "
-                      f"{c.NHQ}+{c.NHK} heads) in {el:.1f} s; numpy fp64, BLAS threads = "
-                      f"{threads}"}
+                      f"{c.NHQ}+{c.NHK} heads) in {el:.1f} s; numpy fp64 elementwise "
+                      f"arithmetic (one thread)"}
 
 
 def time_steps(step, steps: int, warmup: int, eager: bool, spread: list = None,
                settle: dict = None):
     """Warm up, then time exactly `steps` calls of step(i) with events on the
     stream they run on. Returns (device ms, wall s, launch mode). With a dict
-    in `settle`, the captured K-step graph is replayed once, untimed, before
-    the timed replay (the first replay of a heavy workload runs at a lower
-    clock: prefill_8k 11% slower than the next ones on MI355X) and its device
-    ms per step is stored under "first_replay_ms_per_step". With a list in
-    `spread`, the graph is then replayed SPREAD_REPLAYS more times and the
-    timed replay's and each further replay's device ms per step go there."""
+    in `settle`, the captured K-step graph is replayed, untimed, until at
+    least SETTLE_MS of device time has passed, before the timed replay: the
+    clock ramps up over the first tens of milliseconds of sustained load
+    (prefill_8k's first replay is 11% slower than the next ones on MI355X, and
+    a 3 ms decode graph takes about eight replays to settle). The first
+    replay's device ms per step is stored under "first_replay_ms_per_step" and
+    the number of settle replays under "replays". With a list in `spread`,
+    the graph is then replayed SPREAD_REPLAYS more times and the timed
+    replay's and each further replay's device ms per step go there."""
     import torch
 
     for i in range(warmup):
@@ -330,11 +338,18 @@ def time_steps(step, steps: int, warmup: int, eager: bool, spread: list = None,
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     if settle is not None:
-        e0.record()
-        g_main.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        settle["first_replay_ms_per_step"] = e0.elapsed_time(e1) / steps
+        settled_ms, n = 0.0, 0
+        while n == 0 or (settled_ms < SETTLE_MS and n < SETTLE_MAX_REPLAYS):
+            e0.record()
+            g_main.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            if n == 0:
+                settle["first_replay_ms_per_step"] = ms / steps
+            settled_ms += ms
+            n += 1
+        settle["replays"] = n
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record()
@@ -361,6 +376,18 @@ def percentiles(xs: list) -> dict:
     return {"us_median": round(float(np.median(a)), 2),
             "us_p10": round(float(np.percentile(a, 10)), 2),
             "us_p90": round(float(np.percentile(a, 90)), 2), "replays": len(xs)}
+
+
+def timed(step, args):
+    """time_steps with the settle replays and the spread of further replays;
+    returns (device ms, wall s, launch mode, config fields)."""
+    spread, settle = [], {}
+    gpu_ms, wall, launch = time_steps(step, args.steps, args.warmup, args.eager, spread, settle)
+    info = percentiles(spread) if spread else {}
+    if "first_replay_ms_per_step" in settle:
+        info["first_replay_us"] = round(settle["first_replay_ms_per_step"] * 1e3, 2)
+        info["settle_replays"] = settle["replays"]
+    return gpu_ms, wall, launch, info
 
 
 def blas_time_us(T: int, N: int, H: int, fp16: bool, steps: int, warmup: int) -> float:
@@ -454,7 +481,7 @@ def run_qk(args) -> int:
                                      c.eps, range_errors=err):
             raise RuntimeError("QK call fell back")
 
-    gpu_ms, wall, launch = time_steps(step, args.steps, args.warmup, args.eager)
+    gpu_ms, wall, launch, tinfo = timed(step, args)
     assert int(err.item()) == 0
     log(f"[bench] {args.steps} steps: device {gpu_ms:.3f} ms, wall {wall * 1e3:.3f} ms")
     ms_per_step = gpu_ms / args.steps
@@ -480,6 +507,7 @@ def run_qk(args) -> int:
     if not args.no_cpu_baseline:
         log(f"[bench] timing the CPU oracle for ~{args.cpu_seconds} s")
         out["cpu_baseline"] = qk_cpu_baseline(c, args.cpu_seconds)
+    out["config"].update(tinfo)
     print(json.dumps(out), flush=True)
     return 0
 
@@ -508,7 +536,7 @@ def run_verify(args) -> int:
     def step(i):
         dk.verify_accept(d, t, acc, bon)
 
-    gpu_ms, wall, launch = time_steps(step, args.steps, args.warmup, args.eager)
+    gpu_ms, wall, launch, tinfo = timed(step, args)
     ms_per_step = gpu_ms / args.steps
     t_kernel = ms_per_step * 1e-3
     out = {
@@ -522,7 +550,6 @@ def run_verify(args) -> int:
         "roofline": roofline(alg, t_kernel, args.workload),
     }
     if not args.no_cpu_baseline:
-        from threadpoolctl import threadpool_info
         from oracle import verify_oracle as V
         reps, t0 = 0, _t.perf_counter()
         while True:
@@ -531,12 +558,13 @@ def run_verify(args) -> int:
             el = _t.perf_counter() - t0
             if el >= args.cpu_seconds:
                 break
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
         out["cpu_baseline"] = {"value": c.B * reps / el, "unit": "requests/s",
-                               "cores": int(threads), "kind": "oracle",
+                               "cores": 1, "kind": "oracle",
                                "sample": f"{reps} passes of the {c.name} batch ({c.B} requests "
-                                         f"x {c.K} drafts) in {el:.1f} s; numpy cumprod"}
+                                         f"x {c.K} drafts) in {el:.1f} s; numpy cumprod "
+                                         f"(one thread)"}
     del np
+    out["config"].update(tinfo)
     print(json.dumps(out), flush=True)
     return 0
 
@@ -573,7 +601,7 @@ def run_proj(args) -> int:
     def step(i):
         dk.main_proj_norm(packs[i % copies], aux, ctx, ws)
 
-    gpu_ms, wall, launch = time_steps(step, args.steps, args.warmup, args.eager)
+    gpu_ms, wall, launch, tinfo = timed(step, args)
     ms_per_step = gpu_ms / args.steps
     t_kernel = ms_per_step * 1e-3
     out = {
@@ -588,7 +616,6 @@ def run_proj(args) -> int:
         "roofline": roofline(alg, t_kernel, args.workload),
     }
     if not args.no_cpu_baseline:
-        from threadpoolctl import threadpool_info
         from oracle import main_proj_oracle as M
         reps, t0 = 0, time.perf_counter()
         while True:
@@ -597,14 +624,16 @@ def run_proj(args) -> int:
             el = time.perf_counter() - t0
             if el >= args.cpu_seconds:
                 break
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-        out["cpu_baseline"] = {"value": c.T * reps / el, "unit": "tokens/s", "cores": int(threads),
-                               "kind": "oracle",
+        threads, affinity = blas_cores()
+        out["cpu_baseline"] = {"value": c.T * reps / el, "unit": "tokens/s",
+                               "cores": min(threads, affinity), "kind": "oracle",
                                "sample": f"{reps} full passes of the {c.name} batch ({c.T} "
-                                         f"tokens) in {el:.1f} s; numpy fp64, BLAS threads = "
-                                         f"{threads}"}
+                                         f"tokens) in {el:.1f} s; numpy fp64 with BLAS dgemm "
+                                         f"({threads} threads on {affinity} cores in the "
+                                         f"process's affinity mask)"}
     for p in packs:
         p.free()
+    out["config"].update(tinfo)
     print(json.dumps(out), flush=True)
     return 0
 
@@ -649,7 +678,7 @@ def run_attn(args) -> int:
                                   c.max_prefix, ws, err):
             raise RuntimeError("attention fell back")
 
-    gpu_ms, wall, launch = time_steps(step, args.steps, args.warmup, args.eager)
+    gpu_ms, wall, launch, tinfo = timed(step, args)
     assert int(err.item()) == 0
     ms_per_step = gpu_ms / args.steps
     t_kernel = ms_per_step * 1e-3
@@ -666,7 +695,6 @@ def run_attn(args) -> int:
         "roofline": roofline(alg, t_kernel, args.workload),
     }
     if not args.no_cpu_baseline:
-        from threadpoolctl import threadpool_info
         from oracle import draft_attention_oracle as A
         reps, t0 = 0, time.perf_counter()
         while True:  # one request per pass (the whole batch would take minutes)
@@ -679,13 +707,15 @@ def run_attn(args) -> int:
             el = time.perf_counter() - t0
             if el >= args.cpu_seconds:
                 break
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        threads, affinity = blas_cores()
         out_line["cpu_baseline"] = {
-            "value": c.block * reps / el, "unit": "query tokens/s", "cores": int(threads),
+            "value": c.block * reps / el, "unit": "query tokens/s",
+            "cores": min(threads, affinity),
             "kind": "oracle",
             "sample": f"{reps} requests of the {c.name} batch ({c.block} queries, "
                       f"{c.max_prefix}-key prefix each) in {el:.1f} s; numpy fp64, BLAS "
                       f"threads = {threads}"}
+    out_line["config"].update(tinfo)
     print(json.dumps(out_line), flush=True)
     return 0
 
@@ -801,6 +831,7 @@ def run_write(name: str, args, cpu: bool = False, blas: bool = False) -> dict:
         "spread": percentiles(spread) if spread else None,
         "first_replay_us": (round(settle["first_replay_ms_per_step"] * 1e3, 2)
                             if "first_replay_ms_per_step" in settle else None),
+        "settle_replays": settle.get("replays"),
         "roofline": roofline(exe, t_kernel, name),
     }
     for p in packs:
@@ -834,6 +865,7 @@ def config_entry(rec: dict) -> dict:
         e.update(rec["spread"])
     if rec.get("first_replay_us") is not None:
         e["first_replay_us"] = rec["first_replay_us"]
+        e["settle_replays"] = rec.get("settle_replays")
     if "hipblaslt_us" in rec:
         e["hipblaslt_bare_gemm_us"] = rec["hipblaslt_us"]
         e["vs_hipblaslt_bare_gemm"] = round(rec["hipblaslt_us"] / (rec["ms_per_step"] * 1e3), 3)
@@ -868,8 +900,9 @@ def headline_line(rec: dict, args) -> dict:
     if rec.get("spread"):
         out["config"].update(rec["spread"])
     if rec.get("first_replay_us") is not None:
-        # one untimed replay of the K-step graph precedes the timed one
-        out["config"]["settle_replays"] = 1
+        # untimed replays of the K-step graph (at least SETTLE_MS of device
+        # time) precede the timed one
+        out["config"]["settle_replays"] = rec.get("settle_replays")
         out["config"]["first_replay_us"] = rec["first_replay_us"]
     if "cpu_baseline" in rec:
         out["cpu_baseline"] = rec["cpu_baseline"]
