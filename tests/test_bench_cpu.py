@@ -101,3 +101,20 @@ def test_default_run_is_every_write_config_with_prefill_headline():
     assert bench.HEADLINE == "prefill_8k" and bench.HEADLINE in bench.WRITE_CONFIGS
     assert {"tiny", "decode_commit", "prefill_8k", "biased_fp16",
             "wide_gqa_d64"} <= set(bench.WRITE_CONFIGS)
+
+
+def test_weight_copies_exceed_twice_the_infinity_cache():
+    """Rotating weight copies keep every step's weight out of the 256 MB
+    Infinity Cache: their total exceeds twice its size, up to 64 copies."""
+    mb = 1 << 20
+    decode = 10240 * 4096 * 2  # decode_commit / prefill_8k stacked weight, 84 MB
+    assert bench.weight_copies(decode) == 7 and 7 * decode > 2 * 256 * mb
+    kv1 = 1280 * 4096 * 2
+    n = bench.weight_copies(kv1)
+    assert n * kv1 > 2 * 256 * mb and (n - 1) * kv1 <= 2 * 256 * mb
+    assert bench.weight_copies(512 * 256 * 2) == 64  # tiny: capped
+    assert bench.weight_copies(4 << 30) == 1
+
+
+def test_settle_covers_the_clock_ramp():
+    assert bench.SETTLE_MS >= 30.0 and bench.SETTLE_MAX_REPLAYS >= 1
