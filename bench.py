@@ -238,11 +238,11 @@ def blas_probe(args) -> int:
     def step(i):
         torch.matmul(x, wts[i % copies], out=out)
 
-    gpu_ms, _, launch = time_steps(step, args.steps, args.warmup, args.eager)
+    gpu_ms, _, launch, tinfo = timed(step, args)
     t = gpu_ms * 1e-3 / args.steps
     print(json.dumps({"blas_probe": args.workload, "gemm": [T, N, H], "dtype": str(dt),
                       "weight_copies": copies, "launch": launch, "us": round(t * 1e6, 2),
-                      "tflops": round(2.0 * T * N * H / t / 1e12, 1)}))
+                      "tflops": round(2.0 * T * N * H / t / 1e12, 1), **tinfo}))
     return 0
 
 
@@ -295,6 +295,73 @@ def qk_cpu_baseline(c, seconds: float) -> dict:
             "sample": f"{reps} full passes of the {c.name} batch ({c.T} tokens, "
                       f"{c.NHQ}+{c.NHK} heads) in {el:.1f} s; numpy fp64 elementwise "
                       f"arithmetic (one thread)"}
+
+
+class ClockSampler:
+    """Samples the GPU's current shader clock (the amdgpu driver's pp_dpm_sclk,
+    the line marked '*') and board power (hwmon power1_input) from a host
+    thread every ~2 ms while the timed replays run: the clock the kernels
+    actually ran at. Does nothing unless the machine shows exactly one GPU
+    in sysfs."""
+
+    def __init__(self):
+        import glob
+        cards = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.sclk = cards[0] if len(cards) == 1 else None
+        power = glob.glob(os.path.join(os.path.dirname(cards[0]), "hwmon", "*", "power1_input")) \
+            if self.sclk else []
+        self.power = power[0] if power else None
+        self.mhz, self.watts, self._stop, self._thread = [], [], None, None
+
+    @staticmethod
+    def current_mhz(text: str):
+        """The clock of the line pp_dpm_sclk marks with '*' (None if none)."""
+        import re
+        for line in text.splitlines():
+            if line.rstrip().endswith("*"):
+                m = re.search(r"(\d+)\s*[Mm]hz", line)
+                if m:
+                    return int(m.group(1))
+        return None
+
+    def _read(self):
+        try:
+            with open(self.sclk) as f:
+                mhz = self.current_mhz(f.read())
+            if mhz is not None:
+                self.mhz.append(mhz)
+            if self.power:
+                with open(self.power) as f:
+                    self.watts.append(int(f.read().strip()) / 1e6)
+        except (OSError, ValueError):
+            pass
+
+    def start(self):
+        if not self.sclk:
+            return
+        import threading
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.wait(0.002):
+                self._read()
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+
+    def stop(self) -> dict:
+        if not self._thread:
+            return {}
+        self._stop.set()
+        self._thread.join()
+        import numpy as np
+        out = {}
+        if self.mhz:
+            a = np.asarray(self.mhz, dtype=np.float64)
+            out["sclk_mhz"] = {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+                               "p90": float(np.percentile(a, 90)), "samples": int(a.size)}
+        if self.watts:
+            out["board_power_w_median"] = round(float(np.median(self.watts)), 1)
+        return out
 
 
 def time_steps(step, steps: int, warmup: int, eager: bool, spread: list = None,
@@ -351,6 +418,9 @@ def time_steps(step, steps: int, warmup: int, eager: bool, spread: list = None,
             n += 1
         settle["replays"] = n
     torch.cuda.synchronize()
+    sampler = ClockSampler() if settle is not None else None
+    if sampler:
+        sampler.start()
     t0 = time.perf_counter()
     e0.record()
     g_main.replay()
@@ -366,6 +436,8 @@ def time_steps(step, steps: int, warmup: int, eager: bool, spread: list = None,
             torch.cuda.synchronize()
             spread.append(e0.elapsed_time(e1) / steps)
         log("[bench] per-step ms of each replay: " + " ".join(f"{x:.4f}" for x in spread))
+    if sampler:
+        settle["clock"] = sampler.stop()
     return total, wall, "hip_graph"
 
 
@@ -387,14 +459,17 @@ def timed(step, args):
     if "first_replay_ms_per_step" in settle:
         info["first_replay_us"] = round(settle["first_replay_ms_per_step"] * 1e3, 2)
         info["settle_replays"] = settle["replays"]
+    info.update(settle.get("clock") or {})
     return gpu_ms, wall, launch, info
 
 
-def blas_time_us(T: int, N: int, H: int, fp16: bool, steps: int, warmup: int) -> float:
+def blas_time_us(T: int, N: int, H: int, fp16: bool, steps: int, warmup: int,
+                 clock: dict = None) -> float:
     """hipBLASLt (torch.matmul) on the bare GEMM Y [T, N] = X [T, H] @ W^T, timed
     like the write (HIP graph, events on the launch stream) with rotating
     weight copies that exceed the Infinity Cache, so each step reads its
-    weight from HBM. No norm, rotation or scatter."""
+    weight from HBM. No norm, rotation or scatter. The clock sampled during
+    its timed replays goes to `clock`."""
     import torch
 
     dt = torch.float16 if fp16 else torch.bfloat16
@@ -407,7 +482,10 @@ def blas_time_us(T: int, N: int, H: int, fp16: bool, steps: int, warmup: int) ->
     def step(i):
         torch.matmul(x, wts[i % copies], out=out)
 
-    ms, _, _ = time_steps(step, steps, warmup, False, settle={})
+    settle = {}
+    ms, _, _ = time_steps(step, steps, warmup, False, settle=settle)
+    if clock is not None:
+        clock.update(settle.get("clock") or {})
     del x, wts, out
     torch.cuda.empty_cache()
     return ms * 1e3 / steps
@@ -832,6 +910,7 @@ def run_write(name: str, args, cpu: bool = False, blas: bool = False) -> dict:
         "first_replay_us": (round(settle["first_replay_ms_per_step"] * 1e3, 2)
                             if "first_replay_ms_per_step" in settle else None),
         "settle_replays": settle.get("replays"),
+        "clock": settle.get("clock") or {},
         "roofline": roofline(exe, t_kernel, name),
     }
     for p in packs:
@@ -839,8 +918,10 @@ def run_write(name: str, args, cpu: bool = False, blas: bool = False) -> dict:
     del packs, dc, ws
     torch.cuda.empty_cache()
     if blas:
+        bclock = {}
         rec["hipblaslt_us"] = round(blas_time_us(case.T, case.n_tot, case.H, case.dtype == "fp16",
-                                                 args.steps, args.warmup), 2)
+                                                 args.steps, args.warmup, bclock), 2)
+        rec["hipblaslt_clock"] = bclock
     if cpu:
         log(f"[bench] timing the CPU oracle for ~{args.cpu_seconds} s")
         rec["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
@@ -866,8 +947,13 @@ def config_entry(rec: dict) -> dict:
     if rec.get("first_replay_us") is not None:
         e["first_replay_us"] = rec["first_replay_us"]
         e["settle_replays"] = rec.get("settle_replays")
+    e.update(rec.get("clock") or {})
     if "hipblaslt_us" in rec:
         e["hipblaslt_bare_gemm_us"] = rec["hipblaslt_us"]
+        if rec.get("hipblaslt_clock", {}).get("sclk_mhz"):
+            e["hipblaslt_sclk_mhz_median"] = rec["hipblaslt_clock"]["sclk_mhz"]["median"]
+        if rec.get("hipblaslt_clock", {}).get("board_power_w_median"):
+            e["hipblaslt_board_power_w_median"] = rec["hipblaslt_clock"]["board_power_w_median"]
         e["vs_hipblaslt_bare_gemm"] = round(rec["hipblaslt_us"] / (rec["ms_per_step"] * 1e3), 3)
     return e
 
@@ -904,6 +990,7 @@ def headline_line(rec: dict, args) -> dict:
         # time) precede the timed one
         out["config"]["settle_replays"] = rec.get("settle_replays")
         out["config"]["first_replay_us"] = rec["first_replay_us"]
+    out["config"].update(rec.get("clock") or {})
     if "cpu_baseline" in rec:
         out["cpu_baseline"] = rec["cpu_baseline"]
     return out
@@ -923,9 +1010,11 @@ def run_all(args) -> int:
     out["measured_peak"] = {
         **ceil,
         "hipblaslt_bare_gemm_us": head.get("hipblaslt_us"),
+        "sclk_mhz_under_load": (head.get("clock") or {}).get("sclk_mhz", {}).get("median"),
         "note": "second denominators measured in this run: hipBLASLt (torch.matmul) on each "
                 "workload's bare GEMM with rotating weights (configs.*.hipblaslt_bare_gemm_us), "
-                "and torch's 1 GiB copy and sum kernels for HBM",
+                "and torch's 1 GiB copy and sum kernels for HBM; the shader clock sampled from "
+                "the driver during the headline's timed replays (the peaks assume 2.4 GHz)",
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -118,3 +118,11 @@ def test_weight_copies_exceed_twice_the_infinity_cache():
 
 def test_settle_covers_the_clock_ramp():
     assert bench.SETTLE_MS >= 30.0 and bench.SETTLE_MAX_REPLAYS >= 1
+
+
+def test_clock_sampler_reads_the_marked_level():
+    """pp_dpm_sclk lists the clock levels and marks the current one with '*'
+    (an 'S:' line when the clock sits between levels)."""
+    assert bench.ClockSampler.current_mhz("S: 95Mhz *\n0: 500Mhz\n1: 2400Mhz\n") == 95
+    assert bench.ClockSampler.current_mhz("0: 500Mhz\n1: 2100Mhz *\n") == 2100
+    assert bench.ClockSampler.current_mhz("0: 500Mhz\n1: 2400Mhz\n") is None
