@@ -80,18 +80,11 @@ struct Elem<true> {  // fp16
   }
 };
 
-// 16-byte load through a global-address-space pointer: the compiler emits
+// 16-byte nontemporal load of a streamed weight fragment: on a pure HBM
+// stream this reaches about 9% more bandwidth than a default load. The
+// pointer is cast to the global address space so that the compiler emits
 // global_load (counted by vmcnt only) rather than flat_load, which would also
 // hold up every LDS wait behind outstanding memory loads.
-__device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
-  const u32x4 v = *(global_u32x4*)p;
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
-// 16-byte nontemporal load of a streamed weight fragment: on a pure HBM
-// stream this reaches about 9% more bandwidth than a default load.
 __device__ __forceinline__ uint4 ldg16_nt(const uint16_t* p) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
