@@ -8,7 +8,6 @@ pins are then run as plain functions. A mutation that a pin does not notice
 would mean the oracle is not pinned where that mistake lives.
 """
 
-import itertools
 import os
 import sys
 
@@ -19,39 +18,15 @@ from oracle import ctx_kv_oracle as O
 
 sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
 import test_oracle_pins as P  # noqa: E402
+from mutation_util import failing_pins  # noqa: E402
 
 ORIG = {name: getattr(O, name) for name in (
     "round_to", "kv_proj_only", "rms_normalize", "apply_k_norm", "neox_rotate", "apply_k_rope",
     "valid_rows", "layer_kv")}
 
 
-def _pin_calls():
-    """Every pin with every parameter set its parametrize marks give."""
-    for name, fn in sorted(vars(P).items()):
-        if not name.startswith("test_") or not callable(fn):
-            continue
-        grids = []
-        for m in getattr(fn, "pytestmark", []):
-            if m.name != "parametrize":
-                continue
-            names = m.args[0]
-            names = [a.strip() for a in names.split(",")] if isinstance(names, str) else list(names)
-            grids.append([dict(zip(names, v if len(names) > 1 else (v,))) for v in m.args[1]])
-        for combo in itertools.product(*grids):
-            kw = {}
-            for c in combo:
-                kw.update(c)
-            yield name, fn, kw
-
-
 def _failing_pins():
-    failed = []
-    for name, fn, kw in _pin_calls():
-        try:
-            fn(**kw)
-        except Exception:  # an assertion, or the mutated oracle breaking outright
-            failed.append(name)
-    return failed
+    return failing_pins(P)
 
 
 # ------------------------------------------------------------------ mutations

@@ -151,6 +151,21 @@ def test_fp32_weights_equal_patterns_of_the_same_values():
     assert np.array_equal(a, b)
 
 
+def test_fp32_weights_keep_values_outside_the_fp16_range():
+    """fp32 weights of 2^-30 times bf16 values (exact in fp32 and bf16, far
+    below fp16's smallest subnormal) give the same bits as the bf16 patterns
+    of those values: an fp32 weight is used at its own value, not narrowed."""
+    c = W.make_qk_case(T=9, NHQ=2, NHK=1, D=64, seed=12)
+    qv = O.decode(c.q_w, "bf16") * 2.0 ** -30
+    kv = O.decode(c.k_w, "bf16") * 2.0 ** -30
+    a, _ = _run(c.qkv, c.positions, W.to_bits(qv, "bf16"), W.to_bits(kv, "bf16"), c.table, 2, 1,
+                64, eps=c.eps)
+    b, _ = _run(c.qkv, c.positions, qv.astype(np.float32), kv.astype(np.float32), c.table, 2, 1,
+                64, eps=c.eps, weight_dtype="fp32")
+    assert np.array_equal(a, b)
+    assert np.count_nonzero(O.decode(a[:, :192], "bf16")) > 0.9 * a[:, :192].size
+
+
 def test_key_heads_agree_with_the_write_oracle():
     """Consistency with the stacked write's oracle (same arithmetic, other
     entry point): the key heads equal apply_k_rope(apply_k_norm(...))."""
