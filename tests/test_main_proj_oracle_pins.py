@@ -97,3 +97,15 @@ def test_fp32_norm_weight_equals_patterns_of_the_same_values():
     gf = O.decode(c.g, "fp16").astype(np.float32)
     assert np.array_equal(M.main_norm(y, c.g, "fp16", c.eps, "fp16"),
                           M.main_norm(y, gf, "fp32", c.eps, "fp16"))
+
+
+def test_fp32_norm_weight_keeps_values_outside_the_fp16_range():
+    """fp32 norm weights of 2^-30 times bf16 values (exact in fp32 and bf16,
+    below fp16's smallest subnormal) give the same bits as the bf16 patterns
+    of those values, and nonzero outputs."""
+    c = W.make_proj_case(T=5, H=128, n_aux=2, seed=9)
+    y = M.main_proj(c.aux, c.w, "bf16")
+    gv = O.decode(c.g, "bf16") * 2.0 ** -30
+    a = M.main_norm(y, W.to_bits(gv, "bf16"), "bf16", c.eps, "bf16")
+    assert np.array_equal(a, M.main_norm(y, gv.astype(np.float32), "fp32", c.eps, "bf16"))
+    assert np.count_nonzero(a) > 0.9 * a.size
