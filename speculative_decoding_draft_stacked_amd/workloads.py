@@ -506,3 +506,64 @@ def attn_workload(name: str) -> AttnCase:
     """The named draft-attention workload with its fixed seed (5000 + index)."""
     seed = 5000 + ATTN_WORKLOAD_ORDER.index(name) + 1
     return make_attn_case(name=name, seed=seed, **ATTN_WORKLOADS[name])
+
+
+# ---------------------------------------------------------------------------
+# One draft step's inputs for the operations chained on one device: the
+# producer's auxiliary hidden states of the requests' prefix tokens (whose
+# context K/V the stacked write stores), the draft block's fused QKV rows
+# (normed and rotated in place, then the block's queries and own keys and
+# values), and the attention over one layer's pool. The write's layer that
+# the attention reads shares its K norm weight and rotary table with the QK op.
+
+
+@dataclasses.dataclass
+class DraftStepCase:
+    name: str
+    dtype: str
+    B: int
+    block: int
+    layer: int              # the write's layer whose pool the attention reads
+    prefix: np.ndarray      # int64 [B] prefix tokens per request
+    proj: ProjCase          # T = prefix.sum() tokens, H features
+    write: Case             # x is the producer's output (not drawn: zeros here)
+    qk: QkCase              # T = B * block draft tokens
+    kv_indptr: np.ndarray   # int64 [B+1]
+    kv_indices: np.ndarray  # int64 [prefix.sum()]: the write's slots of each request's prefix
+    sm_scale: float
+
+
+def make_draft_step(*, name: str = "draft_step", B: int, block: int, prefix, H: int,
+                    n_aux: int = 3, L: int = 2, NH: int = 2, NHQ: int = 8, D: int = 128,
+                    dtype: str = BF16, slots: Optional[int] = None, P: int = 4096,
+                    theta: float = 1e4, sm_scale: Optional[float] = None,
+                    seed: int = 0) -> DraftStepCase:
+    """Draw one draft step from the three generators above (seeds seed,
+    seed + 1, seed + 2). Request b's prefix tokens sit at positions
+    [0, prefix[b]) and the write's rows are the requests' prefixes in request
+    order, stored at the write's random injective slots; the draft block of b
+    sits at positions [prefix[b], prefix[b] + block). The last layer of the
+    write is the attention's. ``sm_scale`` defaults to 1/sqrt(D); a larger
+    one makes each query's output follow its few best-matching keys."""
+    prefix = np.broadcast_to(np.asarray(prefix, dtype=np.int64), (B,)).copy()
+    T = int(prefix.sum())
+    if slots is None:
+        slots = T + 16
+    if int(prefix.max()) + block > P:
+        raise ValueError("the rotary table is shorter than a request's positions")
+    proj = make_proj_case(name=name + "_proj", T=T, H=H, n_aux=n_aux, dtype=dtype, seed=seed)
+    write = make_case(name=name + "_write", T=T, H=H, L=L, NH=NH, D=D, dtype=dtype, theta=theta,
+                      P=P, slots=slots, eps=proj.eps, seed=seed + 1)
+    positions = np.concatenate([np.arange(n, dtype=np.int64) for n in prefix])
+    write = dataclasses.replace(write, x=np.zeros_like(write.x), positions=positions)
+    qk = make_qk_case(name=name + "_qk", T=B * block, NHQ=NHQ, NHK=NH, D=D, dtype=dtype, P=P,
+                      theta=theta, eps=proj.eps, seed=seed + 2)
+    qk_pos = np.concatenate([n + np.arange(block, dtype=np.int64) for n in prefix])
+    layer = L - 1
+    qk = dataclasses.replace(qk, k_w=write.k_norm_w[layer].copy(), table=write.table,
+                             positions=qk_pos)
+    kv_indptr = np.concatenate([[0], np.cumsum(prefix)]).astype(np.int64)
+    return DraftStepCase(name=name, dtype=dtype, B=B, block=block, layer=layer, prefix=prefix,
+                         proj=proj, write=write, qk=qk, kv_indptr=kv_indptr,
+                         kv_indices=write.locs.copy(),
+                         sm_scale=1.0 / np.sqrt(D) if sm_scale is None else sm_scale)

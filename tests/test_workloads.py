@@ -66,3 +66,21 @@ def test_fp16_workload_has_bias():
     c = W.make_case(name="b", seed=1, **dict(W.WORKLOADS["biased_fp16"], H=8, T=32))
     assert c.dtype == "fp16" and c.qkv_b is not None
     assert c.qkv_b[0].shape == (c.q_size + 2 * c.kv,)
+
+
+def test_draft_step_inputs_line_up():
+    """The chained draft step's inputs: the write's rows are the requests'
+    prefixes in order at positions 0..n-1, the attention lists exactly the
+    write's slots per request, the draft block follows each prefix, and the
+    QK op's key norm weight and table are the attention layer's."""
+    s = W.make_draft_step(B=3, block=4, prefix=[5, 0, 9], H=64, L=2, NH=1, NHQ=2, D=64,
+                          seed=3)
+    assert s.write.T == s.proj.T == 14 and s.qk.T == 12
+    assert s.write.positions.tolist() == list(range(5)) + list(range(9))
+    assert s.kv_indptr.tolist() == [0, 5, 5, 14]
+    assert np.array_equal(s.kv_indices, s.write.locs)
+    assert len(set(s.write.locs.tolist())) == 14 and s.write.locs.max() < s.write.slots
+    assert s.qk.positions.tolist() == [5, 6, 7, 8, 0, 1, 2, 3, 9, 10, 11, 12]
+    assert np.array_equal(s.qk.k_w, s.write.k_norm_w[s.layer]) and s.layer == 1
+    assert s.qk.table is s.write.table and s.qk.eps == s.write.eps == s.proj.eps
+    assert not s.write.x.any()  # the producer's output, not drawn
