@@ -103,6 +103,8 @@ class WritePlan(ctypes.Structure):
         ("k_parts", ctypes.c_int32),
         ("compacts", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_int64),
+        ("token_splits", ctypes.c_int64),
+        ("main_splits", ctypes.c_int64),
     ]
 
 
@@ -268,7 +270,8 @@ class Pack:
         return dict(kernel=KERNEL_NAMES.get(p.kernel, str(p.kernel)), token_tile=p.token_tile,
                     workgroups=p.workgroups, reduce_workgroups=p.reduce_workgroups,
                     k_parts=p.k_parts, compacts=bool(p.compacts),
-                    workspace_bytes=p.workspace_bytes)
+                    workspace_bytes=p.workspace_bytes, token_splits=p.token_splits,
+                    main_splits=p.main_splits)
 
     def workspace_bytes(self, num_tokens: int, has_commit: bool) -> int:
         n = ctypes.c_int64(0)

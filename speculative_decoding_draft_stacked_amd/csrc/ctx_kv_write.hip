@@ -576,17 +576,21 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
 // Row compaction for commit windows. Only rows that are written (slot >= 0
 // and inside the request's committed prefix) need projecting, so the rows of
 // a commit window are first numbered in row order over the valid ones, and
-// valid row j goes to token split j % splits, tile slot j / splits: the splits
-// share the valid rows evenly without the host knowing their count. Every
+// valid row j goes to token split j % m, tile slot j / m, where m = splits,
+// or with OVF m = a.main_splits: those splits share the valid rows evenly
+// without the host knowing their count. With OVF, rows past their m * BT
+// slots fill the other (overflow) splits in order, BT each. Every
 // workgroup runs the same scan (T is small on this path). map[slot] = row, or
 // -1 where the slot holds none; returns this split's number of rows. The scan
 // costs every workgroup a pass per 512 rows, so longer windows (up to 32768
 // rows reach this kernel when there are few weight tiles) keep contiguous
 // splits instead.
-template <int BT>
+template <int BT, bool OVF>
 __device__ int compact_rows(const WriteArgs& a, int64_t sp, int splits, int* map, int* wcnt,
                             int tid) {
   constexpr int NT = 512;
+  const int m = OVF && a.main_splits >= 1 && a.main_splits <= splits ? a.main_splits : splits;
+  const int cap = m * BT;  // slots of the main splits
   const int lane = tid & 63;
   const int wave = tid >> 6;
   for (int i = tid; i < BT; i += NT) map[i] = -1;
@@ -599,8 +603,8 @@ __device__ int compact_rows(const WriteArgs& a, int64_t sp, int splits, int* map
       const int64_t committed = a.commit[t / a.W];
       v = (loc >= 0) & ((t % a.W) < committed);
     }
-    const unsigned long long m = __ballot(v);
-    if (lane == 0) wcnt[wave] = __popcll(m);
+    const unsigned long long mask = __ballot(v);
+    if (lane == 0) wcnt[wave] = __popcll(mask);
     __syncthreads();
     int pre = 0, tot = 0;
 #pragma unroll
@@ -610,11 +614,27 @@ __device__ int compact_rows(const WriteArgs& a, int64_t sp, int splits, int* map
       tot += n;
     }
     if (v) {
-      const int j = base + pre + __popcll(m & ((1ull << lane) - 1ull));
-      if (j % splits == sp && j / splits < BT) map[j / splits] = (int)t;
+      const int j = base + pre + __popcll(mask & ((1ull << lane) - 1ull));
+      if constexpr (OVF) {
+        if (j < cap) {
+          if (j % m == sp) map[j / m] = (int)t;
+        } else if (m + (j - cap) / BT == sp) {
+          map[(j - cap) % BT] = (int)t;
+        }
+      } else if (j % splits == sp && j / splits < BT) {
+        map[j / splits] = (int)t;
+      }
     }
     base += tot;
     __syncthreads();
+  }
+  if constexpr (OVF) {
+    if (sp < m) {
+      const int n = base < cap ? base : cap;
+      return n > sp ? (int)((n - sp + m - 1) / m) : 0;
+    }
+    const int n = base - cap - (int)(sp - m) * BT;
+    return n <= 0 ? 0 : (n < BT ? n : BT);
   }
   return base > sp ? (int)((base - sp + splits - 1) / splits) : 0;
 }
@@ -622,10 +642,12 @@ __device__ int compact_rows(const WriteArgs& a, int64_t sp, int splits, int* map
 // Weight-streaming kernel for small T (decode-sized batches). A workgroup
 // owns one 128-row tile of the stacked weight and BT = 32*NB tokens; the host
 // picks the number of token splits so that the whole grid is one round of
-// workgroups. Eight waves, two per SIMD: wave (w, par) owns weight rows
-// [32w, 32w+32) of the tile and the K chunks of parity par (K is split
-// inside the workgroup; the two halves are added through LDS at the end), so
-// each SIMD interleaves two instruction streams.
+// workgroups (OVF: the workgroups of the main splits are one round, those of
+// the overflow splits follow and usually find no rows). Eight waves, two per
+// SIMD: wave (w, par) owns weight rows [32w, 32w+32) of the tile and the K
+// chunks of parity par (K is split inside the workgroup; the two halves are
+// added through LDS at the end), so each SIMD interleaves two instruction
+// streams.
 //   - Weight: streamed from HBM straight into a per-wave register ring (the
 //     blocked layout gives each MFMA A fragment as one contiguous KiB), with
 //     nontemporal loads.
@@ -637,7 +659,7 @@ __device__ int compact_rows(const WriteArgs& a, int64_t sp, int splits, int* map
 //   - Commit windows: the workgroup's tokens are its share of the written rows
 //     (compact_rows); 32-token blocks past that share skip their MFMAs, and
 //     tile slots without a row load from the zero page.
-template <bool FP16, int D, bool BIAS, bool COMMIT, int NB>
+template <bool FP16, int D, bool BIAS, bool COMMIT, int NB, bool OVF = false>
 __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, int splits) {
   using E = Elem<FP16>;
   using vec8 = typename E::vec8;
@@ -681,14 +703,28 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
   int64_t kq = (int64_t)blockIdx.x / (R * splits);
   const int64_t b = (int64_t)blockIdx.x % (R * splits);
   int64_t rt, sp;
+  // OVF (compacting commit windows, K split): the first msp token splits
+  // share the written rows, the others take rows past their capacity only
+  // and are launched after them
+  const int msp = OVF && a.main_splits >= 1 && a.main_splits <= splits ? a.main_splits : splits;
   if (D != kRowsOut && ks > 1) {
     // the write's K parts: the token splits of one (row tile, K part) slice
     // are 8 workgroups apart, i.e. on one XCD, whose L2 then fetches the
     // weight slice once for all of them; the grid is padded to whole groups
-    // of 8 slices
-    const int64_t slice = ((int64_t)blockIdx.x / (8 * splits)) * 8 + blockIdx.x % 8;
+    // of 8 slices (OVF: the main splits' workgroups first)
+    int64_t bb = blockIdx.x;
+    int nsp = splits, sp0 = 0;
+    if constexpr (OVF) {
+      const int64_t main_grid = (R * ks + 7) / 8 * 8 * msp;
+      const bool over = bb >= main_grid;
+      bb = over ? bb - main_grid : bb;
+      nsp = over ? splits - msp : msp;
+      sp0 = over ? msp : 0;
+    }
+    // (main_grid is a multiple of 8: bb % 8 == blockIdx.x % 8)
+    const int64_t slice = (bb / (8 * nsp)) * 8 + blockIdx.x % 8;
     if (slice >= R * ks) return;  // padding
-    sp = ((int64_t)blockIdx.x / 8) % splits;
+    sp = sp0 + (bb / 8) % nsp;
     rt = slice / ks;
     kq = slice % ks;
   } else if (R % 8 == 0) {
@@ -738,14 +774,19 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
   };
 
   // Commit windows: the weight loads of the first LOOK groups go out before
-  // the row scan, whose latency they then cover; the X loads follow it.
+  // the row scan, whose latency they then cover; the X loads follow it. A
+  // split past the main ones rarely has rows: it issues the same loads, in
+  // the same order, only after the scan has found some.
   int nbe = NB;  // 32-token blocks that hold rows
   if constexpr (COMMIT) {
+    const bool early = !OVF || sp < msp;
+    if (early) {
 #pragma unroll
-    for (int g = 0; g < LOOK; ++g) issue_w(g, wq[g]);
+      for (int g = 0; g < LOOK; ++g) issue_w(g, wq[g]);
+    }
     int mine;
     if (T <= kCompactMaxRows) {
-      mine = compact_rows<BT>(a, sp, splits, rmap, wcnt, tid);
+      mine = compact_rows<BT, OVF>(a, sp, splits, rmap, wcnt, tid);
     } else {  // the split's contiguous rows; the epilogue applies the window
       for (int i = tid; i < BT; i += NT) rmap[i] = t0 + i < T ? (int)(t0 + i) : -1;
       __syncthreads();
@@ -757,6 +798,10 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
     if (mine == 0) {  // uniform: nothing of this split is written
       wait_vmcnt<0>();
       return;
+    }
+    if (!early) {
+#pragma unroll
+      for (int g = 0; g < LOOK; ++g) issue_w(g, wq[g]);
     }
   }
 #pragma unroll
@@ -1018,8 +1063,13 @@ hipError_t launch_stream_nb(const WriteArgs& a, const WritePlan& p, hipStream_t 
   if (p.grid <= 0 || p.grid > 0x7FFFFFFF || p.reduce_grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   WriteArgs b = a;
   b.ksplits = p.kernel == kKernelStreamKSplit ? p.ksplits : 1;
-  hipLaunchKernelGGL((ctx_kv_stream_kernel<FP16, D, BIAS, COMMIT, NB>), dim3((uint32_t)p.grid),
-                     dim3(512), 0, stream, b, (int)p.splits);
+  b.main_splits = (int32_t)(p.main_splits > 0 ? p.main_splits : p.splits);
+  if (COMMIT && NB == 4 && b.main_splits < p.splits)  // the overflow plan
+    hipLaunchKernelGGL((ctx_kv_stream_kernel<FP16, D, BIAS, COMMIT, NB, COMMIT && NB == 4>),
+                       dim3((uint32_t)p.grid), dim3(512), 0, stream, b, (int)p.splits);
+  else
+    hipLaunchKernelGGL((ctx_kv_stream_kernel<FP16, D, BIAS, COMMIT, NB>), dim3((uint32_t)p.grid),
+                       dim3(512), 0, stream, b, (int)p.splits);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.kernel != kKernelStreamKSplit) return e;
   if constexpr (D != kRowsOut)

@@ -153,7 +153,17 @@ static void check_plans() {
                 if (p.kernel == kKernelStreamKSplit) {
                   CHECK(!rows_out && T <= kCompactMaxRows);
                   CHECK(p.ksplits >= 2 && p.ksplits <= 16);
-                  CHECK(p.ksplits * R * p.splits <= c);
+                  if (p.main_splits == 0) {
+                    CHECK(p.ksplits * R * p.splits <= c);  // one round of workgroups
+                  } else {
+                    // overflow plan: the main splits fill one round and hold
+                    // 3/4 of the window; all splits at most two rounds
+                    CHECK(commit && p.nb == 4 && p.ksplits == 2);
+                    CHECK(p.main_splits >= 1 && p.main_splits < p.splits);
+                    CHECK(p.ksplits * R * p.main_splits <= c);
+                    CHECK(p.ksplits * R * p.splits <= 2 * (int64_t)c);
+                    CHECK(p.main_splits * 128 * 4 >= 3 * T);
+                  }
                   CHECK(p.grid % (8 * p.splits) == 0 && p.grid >= R * p.ksplits * p.splits);
                   CHECK(p.reduce_grid == R * p.splits * p.nb);
                   CHECK(p.splits * 32 * p.nb <= kRowMapInts);
@@ -162,6 +172,7 @@ static void check_plans() {
                   CHECK(ws > 0 && ws % 16 == 0 && ws <= max_write_workspace_bytes(c));
                 } else {
                   CHECK(p.ksplits == 1 && p.reduce_grid == 0 && plan_workspace_bytes(p) == 0);
+                  CHECK(p.main_splits == 0);
                   CHECK(p.grid == R * p.splits);
                   CHECK(p.grid <= (R >= c ? R : c));  // one round of workgroups
                 }

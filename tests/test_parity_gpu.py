@@ -259,6 +259,26 @@ def test_commit_len_edges():
     assert len(dc.touched_slots(0, "k")) == 16
 
 
+@pytest.mark.parametrize("committed", [276, 384, 385, 512])
+def test_overflow_token_split(committed):
+    """A 512-row commit window over 40 weight tiles (the wide_gqa_d64 shape):
+    on 256 compute units the plan has four token splits of 128 slots and two K
+    parts, of which the first three share the written rows and the fourth
+    takes only rows past their 384 slots. 276 and 384 written rows leave it
+    empty, 385 give it one row, a fully committed window 128."""
+    W_, B = 8, 64
+    case = W.make_case(T=512, H=1024, L=5, NH=4, D=128, row_width=W_, slots=600, seed=41)
+    lens = np.full(B, committed // B, dtype=np.int64)
+    lens[: committed % B] += 1
+    case.commit_lens = lens
+    dc, pack, _ = _run(case, f"{committed} of 512 rows committed")
+    plan = pack.plan(case.T, True)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert plan["kernel"] == "stream_ksplit" and plan["k_parts"] == 2, plan
+        assert plan["token_splits"] == 4 and plan["main_splits"] == 3, plan
+    assert len(dc.touched_slots(4, "v")) == committed
+
+
 def test_commit_rows_spread_over_token_splits():
     """Small-T commit windows: only written rows are projected, numbered in row
     order and dealt to the token splits in turn. Eight splits with three rows
