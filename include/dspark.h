@@ -185,9 +185,9 @@ typedef struct {
   int32_t compacts;        /* 1: only the rows that are stored are projected */
   int64_t workspace_bytes; /* device workspace the write needs (0: none) */
   int64_t token_splits;    /* streaming: token splits per weight tile; tiled: token tiles */
-  int64_t main_splits;     /* compacting: token splits that share the stored rows evenly;
-                              the others (launched last) take only rows past their
-                              capacity; = token_splits otherwise */
+  int64_t adaptive;        /* 1: K parts only when the stored rows fit token_splits splits,
+                              else K whole over token_splits x k_parts splits (decided on
+                              the device from the committed rows) */
 } dspark_write_plan;
 
 /* Fills *plan for a write of num_tokens rows (has_commit: commit_lens given).
@@ -198,9 +198,8 @@ int dspark_ctx_kv_plan(const dspark_ctx_kv_pack* pack, int64_t num_tokens, int32
 
 /* Device workspace bytes dspark_ctx_kv_write needs for num_tokens rows
  * (has_commit: commit_lens given): fp32 sums of K parts when the write splits
- * K over workgroups (few weight tiles for the device, at most two rounds of
- * 128 x 128 floats per compute unit plus an 8 KiB row map), else 0.
- * Host-only. */
+ * K over workgroups (few weight tiles for the device, at most 128 x 128 floats
+ * per compute unit plus an 8 KiB row map), else 0. Host-only. */
 int dspark_ctx_kv_workspace_bytes(const dspark_ctx_kv_pack* pack, int64_t num_tokens,
                                   int32_t has_commit, int64_t* bytes);
 
@@ -259,7 +258,7 @@ int dspark_ctx_kv_write(const dspark_ctx_kv_pack* pack, const void* ctx_hidden,
  * Returns as dspark_ctx_kv_write, and DSPARK_E_TOO_LARGE when the write
  * would need more workspace than the scratch holds (nothing enqueued). */
 #define DSPARK_STATIC_SCRATCH_CUS 256
-#define DSPARK_STATIC_SCRATCH_BYTES (2LL * 256 * 128 * 128 * 4 + 2048 * 4)
+#define DSPARK_STATIC_SCRATCH_BYTES (256LL * 128 * 128 * 4 + 2048 * 4)
 int dspark_ctx_kv_write_static(const dspark_ctx_kv_pack* pack, const void* ctx_hidden,
                                int64_t num_tokens, int64_t hidden_row_stride,
                                const int64_t* positions, const int64_t* locs,

@@ -104,7 +104,7 @@ class WritePlan(ctypes.Structure):
         ("compacts", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_int64),
         ("token_splits", ctypes.c_int64),
-        ("main_splits", ctypes.c_int64),
+        ("adaptive", ctypes.c_int64),
     ]
 
 
@@ -271,7 +271,7 @@ class Pack:
                     workgroups=p.workgroups, reduce_workgroups=p.reduce_workgroups,
                     k_parts=p.k_parts, compacts=bool(p.compacts),
                     workspace_bytes=p.workspace_bytes, token_splits=p.token_splits,
-                    main_splits=p.main_splits)
+                    adaptive=bool(p.adaptive))
 
     def workspace_bytes(self, num_tokens: int, has_commit: bool) -> int:
         n = ctypes.c_int64(0)

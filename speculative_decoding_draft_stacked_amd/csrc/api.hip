@@ -15,15 +15,14 @@
 
 #include "internal.h"
 
-// Scratch of dspark_ctx_kv_write_static: the K-split part sums (at most two
-// rounds of 128 x 128 fp32 per compute unit) and row map of one write for up
-// to DSPARK_STATIC_SCRATCH_CUS compute units, in a file-scope device array
-// (each device holds its own copy for the life of the process). Host code
-// uses only the device address that hipGetSymbolAddress returns for it, taken
-// once per device with that device current; the name itself is a host-side
-// stand-in.
+// Scratch of dspark_ctx_kv_write_static: the K-split part sums and row map of
+// one write for up to DSPARK_STATIC_SCRATCH_CUS compute units, in a
+// file-scope device array (each device holds its own copy for the life of the
+// process). Host code uses only the device address that hipGetSymbolAddress
+// returns for it, taken once per device with that device current; the name
+// itself is a host-side stand-in.
 constexpr int64_t kStaticScratchBytes =
-    2 * (int64_t)DSPARK_STATIC_SCRATCH_CUS * 128 * 128 * 4 + dspark::kRowMapInts * 4;
+    (int64_t)DSPARK_STATIC_SCRATCH_CUS * 128 * 128 * 4 + dspark::kRowMapInts * 4;
 static_assert(kStaticScratchBytes == DSPARK_STATIC_SCRATCH_BYTES, "header constant");
 static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
@@ -197,7 +196,7 @@ int dspark_ctx_kv_plan(const dspark_ctx_kv_pack* p, int64_t num_tokens, int32_t 
   plan->compacts = w.compacts ? 1 : 0;
   plan->workspace_bytes = dspark::plan_workspace_bytes(w);
   plan->token_splits = w.splits;
-  plan->main_splits = w.main_splits > 0 ? w.main_splits : w.splits;
+  plan->adaptive = w.adaptive ? 1 : 0;
   return DSPARK_OK;
 }
 

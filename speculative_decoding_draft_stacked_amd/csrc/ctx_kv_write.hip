@@ -576,21 +576,17 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
 // Row compaction for commit windows. Only rows that are written (slot >= 0
 // and inside the request's committed prefix) need projecting, so the rows of
 // a commit window are first numbered in row order over the valid ones, and
-// valid row j goes to token split j % m, tile slot j / m, where m = splits,
-// or with OVF m = a.main_splits: those splits share the valid rows evenly
-// without the host knowing their count. With OVF, rows past their m * BT
-// slots fill the other (overflow) splits in order, BT each. Every
+// valid row j goes to token split j % splits, tile slot j / splits: the splits
+// share the valid rows evenly without the host knowing their count. Every
 // workgroup runs the same scan (T is small on this path). map[slot] = row, or
 // -1 where the slot holds none; returns this split's number of rows. The scan
 // costs every workgroup a pass per 512 rows, so longer windows (up to 32768
 // rows reach this kernel when there are few weight tiles) keep contiguous
 // splits instead.
-template <int BT, bool OVF>
+template <int BT>
 __device__ int compact_rows(const WriteArgs& a, int64_t sp, int splits, int* map, int* wcnt,
                             int tid) {
   constexpr int NT = 512;
-  const int m = OVF && a.main_splits >= 1 && a.main_splits <= splits ? a.main_splits : splits;
-  const int cap = m * BT;  // slots of the main splits
   const int lane = tid & 63;
   const int wave = tid >> 6;
   for (int i = tid; i < BT; i += NT) map[i] = -1;
@@ -603,8 +599,8 @@ __device__ int compact_rows(const WriteArgs& a, int64_t sp, int splits, int* map
       const int64_t committed = a.commit[t / a.W];
       v = (loc >= 0) & ((t % a.W) < committed);
     }
-    const unsigned long long mask = __ballot(v);
-    if (lane == 0) wcnt[wave] = __popcll(mask);
+    const unsigned long long m = __ballot(v);
+    if (lane == 0) wcnt[wave] = __popcll(m);
     __syncthreads();
     int pre = 0, tot = 0;
 #pragma unroll
@@ -614,40 +610,81 @@ __device__ int compact_rows(const WriteArgs& a, int64_t sp, int splits, int* map
       tot += n;
     }
     if (v) {
-      const int j = base + pre + __popcll(mask & ((1ull << lane) - 1ull));
-      if constexpr (OVF) {
-        if (j < cap) {
-          if (j % m == sp) map[j / m] = (int)t;
-        } else if (m + (j - cap) / BT == sp) {
-          map[(j - cap) % BT] = (int)t;
-        }
-      } else if (j % splits == sp && j / splits < BT) {
-        map[j / splits] = (int)t;
-      }
+      const int j = base + pre + __popcll(m & ((1ull << lane) - 1ull));
+      if (j % splits == sp && j / splits < BT) map[j / splits] = (int)t;
     }
     base += tot;
     __syncthreads();
   }
-  if constexpr (OVF) {
-    if (sp < m) {
-      const int n = base < cap ? base : cap;
-      return n > sp ? (int)((n - sp + m - 1) / m) : 0;
-    }
-    const int n = base - cap - (int)(sp - m) * BT;
-    return n <= 0 ? 0 : (n < BT ? n : BT);
-  }
   return base > sp ? (int)((base - sp + splits - 1) / splits) : 0;
+}
+
+// Row compaction of the adaptive K-split plan (windows of at most 2 * NT
+// rows): the valid rows are counted first. When they fit the `splits` token
+// splits (BT slots each), valid row j goes to split j % splits as above and
+// the K parts stay (this workgroup serves split sp_split); otherwise K is
+// kept whole and the splits x ks workgroups of a row tile become as many
+// token splits, row j going to split j % (splits * ks) (this workgroup then
+// serves split sp_whole). A negative split serves no rows. *whole tells which
+// mode; returns this workgroup's row count.
+template <int BT>
+__device__ int compact_rows_adaptive(const WriteArgs& a, int sp_split, int sp_whole, int splits,
+                                     int ks, int* map, int* wcnt, int tid, bool* whole) {
+  constexpr int NT = 512;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  for (int i = tid; i < BT; i += NT) map[i] = -1;
+  bool v[2];
+  unsigned long long mask[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int64_t t = (int64_t)c * NT + tid;
+    v[c] = false;
+    if (t < a.T) {
+      const int64_t loc = a.locs[t];
+      const int64_t committed = a.commit[t / a.W];
+      v[c] = (loc >= 0) & ((t % a.W) < committed);
+    }
+    mask[c] = __ballot(v[c]);
+    if (lane == 0) wcnt[c * (NT / 64) + wave] = __popcll(mask[c]);
+  }
+  __syncthreads();
+  int total = 0;
+#pragma unroll
+  for (int i = 0; i < 2 * (NT / 64); ++i) total += wcnt[i];
+  const bool kwhole = total > splits * BT;
+  const int m = kwhole ? splits * ks : splits;
+  const int me = kwhole ? sp_whole : sp_split;
+  int base = 0;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    int pre = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) {
+      const int n = wcnt[c * (NT / 64) + i];
+      pre += i < wave ? n : 0;
+      tot += n;
+    }
+    if (v[c]) {
+      const int j = base + pre + __popcll(mask[c] & ((1ull << lane) - 1ull));
+      if (j % m == me && j / m < BT) map[j / m] = c * NT + tid;
+    }
+    base += tot;
+  }
+  __syncthreads();
+  *whole = kwhole;
+  return me >= 0 && base > me ? (base - me + m - 1) / m : 0;
 }
 
 // Weight-streaming kernel for small T (decode-sized batches). A workgroup
 // owns one 128-row tile of the stacked weight and BT = 32*NB tokens; the host
 // picks the number of token splits so that the whole grid is one round of
-// workgroups (OVF: the workgroups of the main splits are one round, those of
-// the overflow splits follow and usually find no rows). Eight waves, two per
-// SIMD: wave (w, par) owns weight rows [32w, 32w+32) of the tile and the K
-// chunks of parity par (K is split inside the workgroup; the two halves are
-// added through LDS at the end), so each SIMD interleaves two instruction
-// streams.
+// workgroups. Eight waves, two per SIMD: wave (w, par) owns weight rows
+// [32w, 32w+32) of the tile and the K chunks of parity par (K is split
+// inside the workgroup; the two halves are added through LDS at the end), so
+// each SIMD interleaves two instruction streams. ADAPT (compacted windows,
+// K split): the workgroups keep K whole when the window's written rows do not
+// fit the K-split plan's token splits (compact_rows_adaptive).
 //   - Weight: streamed from HBM straight into a per-wave register ring (the
 //     blocked layout gives each MFMA A fragment as one contiguous KiB), with
 //     nontemporal loads.
@@ -659,7 +696,7 @@ __device__ int compact_rows(const WriteArgs& a, int64_t sp, int splits, int* map
 //   - Commit windows: the workgroup's tokens are its share of the written rows
 //     (compact_rows); 32-token blocks past that share skip their MFMAs, and
 //     tile slots without a row load from the zero page.
-template <bool FP16, int D, bool BIAS, bool COMMIT, int NB, bool OVF = false>
+template <bool FP16, int D, bool BIAS, bool COMMIT, int NB, bool ADAPT = false>
 __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, int splits) {
   using E = Elem<FP16>;
   using vec8 = typename E::vec8;
@@ -677,7 +714,8 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
   constexpr int XBYTES = XSTAGES * SXE * 2;
   constexpr int EBYTES = BT * RS * 4 + BT * LDO * 2;
   static_assert(XPW * 256 * 8 == SXE, "X chunk split");
-  constexpr int MBYTES = COMMIT ? (BT + NT / 64) * 4 : 0;  // row map + scan counts
+  static_assert(!ADAPT || (COMMIT && D != kRowsOut), "adaptive K split: compacted writes");
+  constexpr int MBYTES = COMMIT ? (BT + (ADAPT ? 2 : 1) * NT / 64) * 4 : 0;  // row map + counts
   __shared__ __align__(16) uint16_t smem[((XBYTES > EBYTES ? XBYTES : EBYTES) + MBYTES) / 2];
   int* const rmap = reinterpret_cast<int*>(smem + (XBYTES > EBYTES ? XBYTES : EBYTES) / 2);
   int* const wcnt = rmap + BT;
@@ -699,34 +737,28 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
   // part b / (R * splits) and writes fp32 partial sums instead of the
   // epilogue; the producer's row-norm kernel, or ctx_kv_stream_reduce for the
   // write, adds the parts.
-  const int ks = a.ksplits > 1 ? a.ksplits : 1;
+  int ks = a.ksplits > 1 ? a.ksplits : 1;
   int64_t kq = (int64_t)blockIdx.x / (R * splits);
   const int64_t b = (int64_t)blockIdx.x % (R * splits);
   int64_t rt, sp;
-  // OVF (compacting commit windows, K split): the first msp token splits
-  // share the written rows, the others take rows past their capacity only
-  // and are launched after them
-  const int msp = OVF && a.main_splits >= 1 && a.main_splits <= splits ? a.main_splits : splits;
   if (D != kRowsOut && ks > 1) {
     // the write's K parts: the token splits of one (row tile, K part) slice
     // are 8 workgroups apart, i.e. on one XCD, whose L2 then fetches the
     // weight slice once for all of them; the grid is padded to whole groups
-    // of 8 slices (OVF: the main splits' workgroups first)
-    int64_t bb = blockIdx.x;
-    int nsp = splits, sp0 = 0;
-    if constexpr (OVF) {
-      const int64_t main_grid = (R * ks + 7) / 8 * 8 * msp;
-      const bool over = bb >= main_grid;
-      bb = over ? bb - main_grid : bb;
-      nsp = over ? splits - msp : msp;
-      sp0 = over ? msp : 0;
+    // of 8 slices
+    if constexpr (!ADAPT) {
+      const int64_t slice = ((int64_t)blockIdx.x / (8 * splits)) * 8 + blockIdx.x % 8;
+      if (slice >= R * ks) return;  // padding
+      sp = ((int64_t)blockIdx.x / 8) % splits;
+      rt = slice / ks;
+      kq = slice % ks;
+    } else {  // padding takes part in the scan (it may serve rows with K whole)
+      const int64_t slice = ((int64_t)blockIdx.x / (8 * splits)) * 8 + blockIdx.x % 8;
+      const bool pad = slice >= R * ks;
+      sp = pad ? -1 : ((int64_t)blockIdx.x / 8) % splits;
+      rt = pad ? 0 : slice / ks;
+      kq = pad ? 0 : slice % ks;
     }
-    // (main_grid is a multiple of 8: bb % 8 == blockIdx.x % 8)
-    const int64_t slice = (bb / (8 * nsp)) * 8 + blockIdx.x % 8;
-    if (slice >= R * ks) return;  // padding
-    sp = sp0 + (bb / 8) % nsp;
-    rt = slice / ks;
-    kq = slice % ks;
   } else if (R % 8 == 0) {
     const int64_t i = b / 8;
     rt = 8 * (i / splits) + b % 8;
@@ -735,13 +767,13 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
     rt = b / splits;
     sp = b % splits;
   }
-  const int64_t n0 = rt * BN;
+  int64_t n0 = rt * BN;
   const int64_t t0 = sp * BT;
   const int nk_all = (H + BK - 1) / BK;
-  const int kc0 = (int)(kq * nk_all / ks);         // this part's chunks [kc0, kc1)
-  const int nk = (int)((kq + 1) * nk_all / ks) - kc0;
-  const int ng = (nk + 1) / 2;
-  const int ng_ring = (ng + SLOTS - 1) / SLOTS * SLOTS;
+  int kc0 = (int)(kq * nk_all / ks);         // this part's chunks [kc0, kc1)
+  int nk = (int)((kq + 1) * nk_all / ks) - kc0;
+  int ng = (nk + 1) / 2;
+  int ng_ring = (ng + SLOTS - 1) / SLOTS * SLOTS;
   // this wave's pieces of weight block (rt, c): one contiguous KiB per MFMA step
   const uint16_t* wblk = a.w + (rt * nk_all + kc0) * 8192 + (w * 4 * 64 + lane) * 8;
   // X direct loads: instruction i of wave (w, par) fills LDS slots
@@ -774,34 +806,55 @@ __global__ __launch_bounds__(512) void ctx_kv_stream_kernel(const WriteArgs a, i
   };
 
   // Commit windows: the weight loads of the first LOOK groups go out before
-  // the row scan, whose latency they then cover; the X loads follow it. A
-  // split past the main ones rarely has rows: it issues the same loads, in
-  // the same order, only after the scan has found some.
+  // the row scan, whose latency they then cover; the X loads follow it.
   int nbe = NB;  // 32-token blocks that hold rows
   if constexpr (COMMIT) {
-    const bool early = !OVF || sp < msp;
-    if (early) {
 #pragma unroll
-      for (int g = 0; g < LOOK; ++g) issue_w(g, wq[g]);
-    }
+    for (int g = 0; g < LOOK; ++g) issue_w(g, wq[g]);
     int mine;
-    if (T <= kCompactMaxRows) {
-      mine = compact_rows<BT, OVF>(a, sp, splits, rmap, wcnt, tid);
+    if (ADAPT && T <= kCompactMaxRows) {
+      // K whole: the R * splits * ks workgroups take the row tiles and token
+      // splits the plain streaming plan would give them (a tile's splits on
+      // one XCD); the others, and the padding, serve no rows
+      const int sw = splits * ks;
+      const int64_t bw = blockIdx.x;
+      const bool in_whole = bw < R * sw;
+      const int64_t rt_w = !in_whole ? 0 : R % 8 == 0 ? 8 * ((bw / 8) / sw) + bw % 8 : bw / sw;
+      const int sp_w = !in_whole ? -1 : (int)(R % 8 == 0 ? (bw / 8) % sw : bw % sw);
+      bool whole;
+      mine = compact_rows_adaptive<BT>(a, (int)sp, sp_w, splits, ks, rmap, wcnt, tid, &whole);
+      if (whole) {  // no part sums: the reduce launch finds no rows
+        if (blockIdx.x == 0)
+          for (int i = tid; i < splits * BT; i += NT) a.rowmap[i] = -1;
+        ks = 1;
+        kq = 0;
+        rt = rt_w;
+        sp = sp_w;
+        n0 = rt * BN;
+        kc0 = 0;
+        nk = nk_all;
+        ng = (nk + 1) / 2;
+        ng_ring = (ng + SLOTS - 1) / SLOTS * SLOTS;
+        wblk = a.w + rt * nk_all * 8192 + (w * 4 * 64 + lane) * 8;
+        if (mine > 0) {  // this tile's K from the start (the scan's loads, issued
+                         // after the ones above, have completed)
+#pragma unroll
+          for (int g = 0; g < LOOK; ++g) issue_w(g, wq[g]);
+        }
+      }
+    } else if (T <= kCompactMaxRows) {
+      mine = compact_rows<BT>(a, sp, splits, rmap, wcnt, tid);
     } else {  // the split's contiguous rows; the epilogue applies the window
       for (int i = tid; i < BT; i += NT) rmap[i] = t0 + i < T ? (int)(t0 + i) : -1;
       __syncthreads();
       mine = (int)(T - t0 < BT ? T - t0 : BT);
     }
     nbe = (mine + 31) / 32;
-    if (D != kRowsOut && ks > 1 && kq == 0 && rt == 0)  // for ctx_kv_stream_reduce
+    if (D != kRowsOut && ks > 1 && kq == 0 && rt == 0 && (!ADAPT || sp >= 0))  // for the reduce
       for (int i = tid; i < BT; i += NT) a.rowmap[sp * BT + i] = rmap[i];
     if (mine == 0) {  // uniform: nothing of this split is written
       wait_vmcnt<0>();
       return;
-    }
-    if (!early) {
-#pragma unroll
-      for (int g = 0; g < LOOK; ++g) issue_w(g, wq[g]);
     }
   }
 #pragma unroll
@@ -1063,13 +1116,19 @@ hipError_t launch_stream_nb(const WriteArgs& a, const WritePlan& p, hipStream_t 
   if (p.grid <= 0 || p.grid > 0x7FFFFFFF || p.reduce_grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   WriteArgs b = a;
   b.ksplits = p.kernel == kKernelStreamKSplit ? p.ksplits : 1;
-  b.main_splits = (int32_t)(p.main_splits > 0 ? p.main_splits : p.splits);
-  if (COMMIT && NB == 4 && b.main_splits < p.splits)  // the overflow plan
-    hipLaunchKernelGGL((ctx_kv_stream_kernel<FP16, D, BIAS, COMMIT, NB, COMMIT && NB == 4>),
-                       dim3((uint32_t)p.grid), dim3(512), 0, stream, b, (int)p.splits);
-  else
+  if (p.adaptive) {  // compacted, K split unless the written rows need K whole
+    if constexpr (COMMIT && NB == 4 && D != kRowsOut) {
+      // (the adaptive scan holds two rows per thread)
+      if (p.kernel != kKernelStreamKSplit || a.T > 1024) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((ctx_kv_stream_kernel<FP16, D, BIAS, COMMIT, NB, true>),
+                         dim3((uint32_t)p.grid), dim3(512), 0, stream, b, (int)p.splits);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else {
     hipLaunchKernelGGL((ctx_kv_stream_kernel<FP16, D, BIAS, COMMIT, NB>), dim3((uint32_t)p.grid),
                        dim3(512), 0, stream, b, (int)p.splits);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.kernel != kKernelStreamKSplit) return e;
   if constexpr (D != kRowsOut)

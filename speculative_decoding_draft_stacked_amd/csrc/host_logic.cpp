@@ -42,24 +42,21 @@ int write_ksplits(int64_t T, int64_t R, int64_t H, int64_t splits, int64_t nb, i
   return (int)ks;
 }
 
-// A commit window too large for the K-split plan above (its workgroups would
-// take two rounds) still gets two K parts when the rows a window commits fit
-// one round: token splits of 128 slots covering every row, of which only the
-// first `main` (as many as one round holds) share the written rows; the rest
-// take rows past 3/4 of the window only, so that on windows committing up to
-// 3/4 of their rows their workgroups find nothing and exit on the CUs the
-// main ones leave idle. Returns the main split count, or 0 when this plan
-// does not apply (it also keeps the part sums within twice one round's).
-int64_t overflow_main_splits(int64_t T, int64_t R, int64_t H, int num_cus) {
+// A commit window whose rows need more token splits than one round of
+// two-K-part workgroups holds: as many token splits of 128 slots as that
+// round holds, when they take 3/4 of the window. The workgroups count the
+// window's written rows first; when those do not fit the splits, the same
+// workgroups keep K whole as splits x 2 token splits, which must hold every
+// row. Returns the token splits, or 0 when this plan does not apply.
+int64_t adaptive_splits(int64_t T, int64_t R, int64_t H, int num_cus) {
   constexpr int64_t kParts = 2, kSlots = 128;
-  const int64_t splits = ceil_div(T, kSlots);
-  if (splits > kKSplitTokenSplits || splits * kSlots > kRowMapInts) return 0;
+  if (T > 2 * 512) return 0;  // the adaptive scan holds two rows per thread
   if (ceil_div(H, kBK) / 8 < kParts) return 0;
-  const int64_t main = num_cus / (R * kParts);
-  if (main < 1 || main >= splits) return 0;
-  if (main * kSlots * 4 < 3 * T) return 0;
-  if (R * kParts * splits > 2 * (int64_t)num_cus) return 0;
-  return main;
+  const int64_t splits = num_cus / (R * kParts);
+  if (splits < 1 || splits * kSlots >= T) return 0;
+  if (splits * kSlots * 4 < 3 * T || splits * kParts * kSlots < T) return 0;
+  if (splits * kSlots > kRowMapInts) return 0;
+  return splits;
 }
 
 }  // namespace
@@ -166,12 +163,12 @@ WritePlan plan_write(int64_t T, int64_t R, int64_t H, bool has_commit, bool rows
     }
     ks = write_ksplits(T, R, H, splits, nb, num_cus);
     if (ks == 1 && has_commit && T <= kCompactMaxRows) {
-      const int64_t main = overflow_main_splits(T, R, H, num_cus);
-      if (main > 0) {
-        splits = ceil_div(T, 128);
+      const int64_t s3 = adaptive_splits(T, R, H, num_cus);
+      if (s3 > 0) {
+        splits = s3;
         nb = 4;
         ks = 2;
-        p.main_splits = main;
+        p.adaptive = true;
       }
     }
   }
@@ -182,8 +179,7 @@ WritePlan plan_write(int64_t T, int64_t R, int64_t H, bool has_commit, bool rows
     p.kernel = kKernelStreamKSplit;
     p.ksplits = ks;
     // the token splits of one (row tile, K part) slice run 8 workgroups
-    // apart (one XCD); the grid is padded to whole groups of 8 slices, the
-    // main splits' workgroups first
+    // apart (one XCD); the grid is padded to whole groups of 8 slices
     p.grid = ceil_div(R * ks, 8) * 8 * splits;
     p.reduce_grid = R * splits * nb;
     p.part_floats = (int64_t)ks * R * splits * 32 * nb * kBN;
@@ -202,9 +198,7 @@ int64_t plan_workspace_bytes(const WritePlan& p) {
 
 int64_t max_write_workspace_bytes(int num_cus) {
   if (num_cus < 1) num_cus = 1;
-  // part sums of at most two rounds of workgroups (the overflow plan), each
-  // 128 x 128 fp32
-  return 2 * (int64_t)num_cus * kBN * kBN * 4 + kRowMapInts * 4;
+  return (int64_t)num_cus * kBN * kBN * 4 + kRowMapInts * 4;
 }
 
 int producer_ksplits(int64_t T, int64_t R, int64_t in_features, int64_t out_features,

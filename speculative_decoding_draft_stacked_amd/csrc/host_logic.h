@@ -45,10 +45,10 @@ struct WritePlan {
   bool compacts = false;    // commit-window rows numbered and projected only when written
   int64_t part_floats = 0;  // workspace: fp32 K-part sums
   int64_t rowmap_ints = 0;  // workspace: committed-row map of the token splits
-  // streaming with compaction: the first main_splits token splits share the
-  // written rows round-robin; rows past their capacity fill the others in
-  // order (0: all splits share)
-  int64_t main_splits = 0;
+  // streaming, compacted, K split: the workgroups keep K whole (splits x
+  // ksplits token splits, no part sums) when the written rows do not fit
+  // `splits` token splits; decided on the device
+  bool adaptive = false;
 };
 
 // Commit windows of at most this many rows are compacted by the streaming

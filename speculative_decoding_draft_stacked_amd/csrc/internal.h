@@ -31,9 +31,6 @@ struct WriteArgs {
   int64_t y_stride;
   int64_t R;                // 128-row tiles of the blocked weight
   int32_t ksplits;          // K parts over workgroups (<= 1: none); set by the launchers
-  int32_t main_splits;      // write, compacting: token splits sharing the written rows
-                            // round-robin (the rest take the rows past their capacity,
-                            // in order); set by the launchers
   int64_t x_stride;
   int64_t T;
   int64_t P;

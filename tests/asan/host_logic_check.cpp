@@ -148,22 +148,20 @@ static void check_plans() {
                 CHECK(cdiv(T, 32) > 4 * (R >= c ? 1 : c / R));
               } else {
                 CHECK(p.nb >= 1 && p.nb <= 4);
-                CHECK(p.splits * p.nb * 32 >= T && (p.splits - 1) * p.nb * 32 < T);
+                if (p.adaptive) {
+                  // the K-split splits hold 3/4 of the window, K-whole ones all of it
+                  CHECK(p.kernel == kKernelStreamKSplit && commit && !rows_out);
+                  CHECK(p.nb == 4 && p.ksplits == 2 && T <= 1024);
+                  CHECK(p.splits * 128 < T && p.splits * 128 * 4 >= 3 * T);
+                  CHECK(p.splits * 128 * p.ksplits >= T);
+                } else {
+                  CHECK(p.splits * p.nb * 32 >= T && (p.splits - 1) * p.nb * 32 < T);
+                }
                 CHECK(p.compacts == (commit && !rows_out && T <= kCompactMaxRows));
                 if (p.kernel == kKernelStreamKSplit) {
                   CHECK(!rows_out && T <= kCompactMaxRows);
                   CHECK(p.ksplits >= 2 && p.ksplits <= 16);
-                  if (p.main_splits == 0) {
-                    CHECK(p.ksplits * R * p.splits <= c);  // one round of workgroups
-                  } else {
-                    // overflow plan: the main splits fill one round and hold
-                    // 3/4 of the window; all splits at most two rounds
-                    CHECK(commit && p.nb == 4 && p.ksplits == 2);
-                    CHECK(p.main_splits >= 1 && p.main_splits < p.splits);
-                    CHECK(p.ksplits * R * p.main_splits <= c);
-                    CHECK(p.ksplits * R * p.splits <= 2 * (int64_t)c);
-                    CHECK(p.main_splits * 128 * 4 >= 3 * T);
-                  }
+                  CHECK(p.ksplits * R * p.splits <= c);
                   CHECK(p.grid % (8 * p.splits) == 0 && p.grid >= R * p.ksplits * p.splits);
                   CHECK(p.reduce_grid == R * p.splits * p.nb);
                   CHECK(p.splits * 32 * p.nb <= kRowMapInts);
@@ -172,7 +170,6 @@ static void check_plans() {
                   CHECK(ws > 0 && ws % 16 == 0 && ws <= max_write_workspace_bytes(c));
                 } else {
                   CHECK(p.ksplits == 1 && p.reduce_grid == 0 && plan_workspace_bytes(p) == 0);
-                  CHECK(p.main_splits == 0);
                   CHECK(p.grid == R * p.splits);
                   CHECK(p.grid <= (R >= c ? R : c));  // one round of workgroups
                 }

@@ -260,12 +260,13 @@ def test_commit_len_edges():
 
 
 @pytest.mark.parametrize("committed", [276, 384, 385, 512])
-def test_overflow_token_split(committed):
+def test_adaptive_k_split(committed):
     """A 512-row commit window over 40 weight tiles (the wide_gqa_d64 shape):
-    on 256 compute units the plan has four token splits of 128 slots and two K
-    parts, of which the first three share the written rows and the fourth
-    takes only rows past their 384 slots. 276 and 384 written rows leave it
-    empty, 385 give it one row, a fully committed window 128."""
+    on 256 compute units the plan has three token splits of 128 slots and two
+    K parts (one round). 276 and 384 written rows fit the three splits (K
+    split, part sums and the reduce launch); 385 and 512 do not, and the same
+    workgroups keep K whole as six token splits (no part sums; the reduce
+    launch finds no rows)."""
     W_, B = 8, 64
     case = W.make_case(T=512, H=1024, L=5, NH=4, D=128, row_width=W_, slots=600, seed=41)
     lens = np.full(B, committed // B, dtype=np.int64)
@@ -275,8 +276,11 @@ def test_overflow_token_split(committed):
     plan = pack.plan(case.T, True)
     if torch.cuda.get_device_properties(0).multi_processor_count == 256:
         assert plan["kernel"] == "stream_ksplit" and plan["k_parts"] == 2, plan
-        assert plan["token_splits"] == 4 and plan["main_splits"] == 3, plan
+        assert plan["token_splits"] == 3 and plan["adaptive"], plan
     assert len(dc.touched_slots(4, "v")) == committed
+    # the same shape with a row count of the other mode
+    case.commit_lens = np.full(B, 8 if committed <= 384 else 4, dtype=np.int64)
+    dc2, _, _ = _run(case, "other mode, same shape")
 
 
 def test_commit_rows_spread_over_token_splits():
