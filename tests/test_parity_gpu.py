@@ -283,6 +283,34 @@ def test_adaptive_k_split(committed):
     dc2, _, _ = _run(case, "other mode, same shape")
 
 
+ADAPTIVE = {
+    # 40 weight tiles each: the adaptive plan on 256 compute units
+    "fp16_bias_d64": dict(T=512, H=1024, L=5, NH=8, D=64, dtype="fp16", bias=True),
+    "bf16_bias_ktail": dict(T=512, H=1096, L=5, NH=4, D=128, bias=True),
+    "fp16_ten_layers": dict(T=512, H=1024, L=10, NH=2, D=128, dtype="fp16"),
+    "bf16_T400": dict(T=400, H=1024, L=5, NH=8, D=64),
+}
+
+
+@pytest.mark.parametrize("mode", ["k_split", "k_whole"])
+@pytest.mark.parametrize("name", list(ADAPTIVE))
+def test_adaptive_k_split_variants(name, mode):
+    """The adaptive plan's kernel instances (dtype, bias, head size, a K tail,
+    a window that is not a multiple of the split size), each with about half
+    of the window committed (K split) and with all of it (K whole)."""
+    kw = ADAPTIVE[name]
+    case = W.make_case(row_width=8, slots=kw["T"] + 100, commit_range=(1, 9),
+                       seed=zlib.crc32(name.encode()) % 10000, **kw)
+    if mode == "k_whole":
+        case.commit_lens = np.full(kw["T"] // 8, 8, dtype=np.int64)
+    dc, pack, _ = _run(case, f"{name} {mode}")
+    plan = pack.plan(case.T, True)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert plan["adaptive"] and plan["token_splits"] == 3, plan
+    written = int(O.valid_rows(case.locs, case.commit_lens, case.row_width).sum())
+    assert (written > 3 * 128) == (mode == "k_whole"), written
+
+
 def test_commit_rows_spread_over_token_splits():
     """Small-T commit windows: only written rows are projected, numbered in row
     order and dealt to the token splits in turn. Eight splits with three rows
