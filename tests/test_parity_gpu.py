@@ -558,3 +558,39 @@ def test_graph_replays_match_eager(H):
         torch.cuda.synchronize()
         k, v = dc.pools_host()
         assert all(np.array_equal(a, b) for a, b in zip(k + v, k_ref + v_ref)), rep
+
+
+def test_adaptive_plan_switches_modes_between_graph_replays():
+    """The adaptive plan captured once in a HIP graph: the commit lengths are
+    device data, so replays alternate between a window that fits the K-split
+    splits (about half committed) and a fully committed one (K whole), each
+    replay matching the eager result of its own commit lengths."""
+    case = W.make_case(T=512, H=1024, L=5, NH=4, D=128, row_width=8, commit_range=(1, 9),
+                       slots=700, seed=57)
+    half = case.commit_lens.copy()
+    full = np.full(64, 8, dtype=np.int64)
+    refs = {}
+    for name, lens in (("half", half), ("full", full)):
+        case.commit_lens = lens
+        dc, pack, _ = _run(case, f"eager, {name} committed")
+        refs[name] = dc.pools_host()
+    assert pack.plan(case.T, True)["adaptive"] or \
+        torch.cuda.get_device_properties(0).multi_processor_count != 256
+    ws = dc.workspace(pack)
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    dc.reset_pools()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            assert dc.write(pack, workspace=ws)
+    for rep, name in enumerate(["half", "full", "half", "full"]):
+        dc.commit.copy_(torch.from_numpy(half if name == "half" else full))
+        for p in dc.pk + dc.pv:
+            p.view(torch.int16).fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        k, v = dc.pools_host()
+        k_ref, v_ref = refs[name]
+        assert all(np.array_equal(a, b) for a, b in zip(k + v, k_ref + v_ref)), (rep, name)
