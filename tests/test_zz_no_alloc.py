@@ -1,8 +1,8 @@
 """dspark_ctx_kv_write_static (the write with the library's static device
 scratch instead of a caller workspace) against dspark_ctx_kv_write, through
 the C ABI: bit-identical pools on two calls in a row, the second smaller,
-both in the K-split form that uses the scratch, plus a write that needs no
-scratch at all."""
+both in the K-split form that uses the scratch, the adaptive plan in both of
+its modes, plus a write that needs no scratch at all."""
 
 import dataclasses
 
@@ -64,6 +64,22 @@ def test_static_scratch_two_calls_second_smaller():
                                 commit_lens=big.commit_lens[:8])
     assert pack.plan(small.T, True)["kernel"] == "stream_ksplit"
     _same_as_workspace_entry(small, pack, "second, smaller call")
+    pack.free()
+
+
+def test_static_entry_adaptive_plan_both_modes():
+    # a 512-row window over 40 weight tiles: the adaptive plan's part sums in
+    # the scratch (about half of the window committed), then the same pack
+    # with every row committed (K whole, the scratch holds only the row map)
+    case = W.make_case(name="static5", seed=84, T=512, H=1024, L=5, NH=4, D=128, row_width=8,
+                       commit_range=(1, 9), slots=700)
+    dc = DeviceCase(case)
+    pack = dc.pack()
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert pack.plan(case.T, True)["adaptive"]
+    _same_as_workspace_entry(case, pack, "adaptive, K split")
+    full = dataclasses.replace(case, name="static6", commit_lens=np.full(64, 8, dtype=np.int64))
+    _same_as_workspace_entry(full, pack, "adaptive, K whole")
     pack.free()
 
 
