@@ -12,7 +12,9 @@ with few weight tiles, H >= 1024 and T <= 1024, which take the K-split form
 shapes for the LDS-tiled kernel: T large enough for its plan, D = 64 tiles
 holding four heads that may span two layers, odd weight-tile counts whose
 last workgroup tile lies half past the stacked weight, bias, commit windows
-and negative slots. Sizes keep the fp64 oracle to about a second per case.
+and negative slots. A fourth draws commit windows for the adaptive K-split
+plan, in both of its modes. Sizes keep the fp64 oracle to about a second per
+case.
 """
 
 import numpy as np
@@ -119,6 +121,57 @@ def test_random_shape_k_split(i):
     torch.cuda.synchronize()
     check_slot_sets(dc)
     st = compare_rows(dc, None, f"ksweep{i}")
+    assert dc.range_errors() == 0
+    say(f"  ok: {st}")
+    pack.free()
+
+
+# ------------------------------------ shapes for the adaptive K-split plan
+
+N_ADAPTIVE_CASES = 10
+# (layers, KV heads, head_dim) giving 20, 32, 40, 64 and 80 weight tiles of
+# 128 rows, i.e. 6, 4, 3, 2 and 1 token splits of 128 slots for two K parts
+# on 256 compute units, with the window sizes each plan covers
+_ADAPTIVE_SHAPES = [((5, 2, 128), 6), ((4, 4, 128), 4), ((5, 8, 64), 3), ((8, 4, 128), 2),
+                    ((5, 8, 128), 1)]
+
+
+def _draw_adaptive(i):
+    """Commit windows too large for one round of K-split workgroups with one
+    128-slot token split per 128 rows, but whose 3/4 fits one round: the
+    adaptive plan. The committed fraction is drawn so that some windows fit
+    the K-split splits and others need K whole."""
+    rng = np.random.default_rng(9800 + i)
+    (L, NH, D), splits = _ADAPTIVE_SHAPES[i % len(_ADAPTIVE_SHAPES)]
+    lo, hi = splits * 128 + 1, min(1024, splits * 128 * 4 // 3)
+    Wd = int(rng.choice([4, 8, 16]))
+    T = int(rng.integers(lo, hi + 1)) // Wd * Wd
+    T = max(T, (lo + Wd - 1) // Wd * Wd)
+    H = int(rng.choice([1024, 1096, 1536]))
+    frac = float(rng.choice([0.4, 0.6, 1.0]))
+    kw = dict(name=f"asweep{i}", T=T, H=H, L=L, NH=NH, D=D,
+              dtype="fp16" if rng.random() < 0.4 else "bf16", bias=bool(rng.random() < 0.4),
+              seed=9800 + i, theta=float(rng.choice([1e4, 1e6])), P=4096, row_width=Wd,
+              commit_range=(max(0, int(frac * Wd) - 2), int(frac * Wd) + 2),
+              neg_loc_frac=float(rng.choice([0.0, 0.05])), slots=T + 37)
+    return kw, splits
+
+
+@pytest.mark.parametrize("i", range(N_ADAPTIVE_CASES))
+def test_random_shape_adaptive(i):
+    kw, splits = _draw_adaptive(i)
+    case = W.make_case(**kw)
+    say(f"[asweep {i}] T={case.T} H={case.H} L={case.L} NH={case.NH} D={case.D} {case.dtype} "
+        f"bias={case.qkv_b is not None} W={case.row_width}")
+    dc = DeviceCase(case)
+    pack = dc.pack()
+    plan = pack.plan(case.T, True)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert plan["adaptive"] and plan["token_splits"] == splits, plan
+    assert dc.write(pack)
+    torch.cuda.synchronize()
+    check_slot_sets(dc)
+    st = compare_rows(dc, None, f"asweep{i}")
     assert dc.range_errors() == 0
     say(f"  ok: {st}")
     pack.free()
