@@ -256,10 +256,44 @@ static void check_row_validation() {
   CHECK(c == DSPARK_RANGE_NONE && row == -1);
 }
 
+// The plans of the benchmark's write workloads on 256 compute units, as the
+// design describes them (R = layers x 2 x KV heads x head_dim / 128).
+static void check_named_plans() {
+  const int cus = 256;
+  // decode_commit: 80 tiles, 256-row window: 3 token splits of 96 slots
+  WritePlan p = plan_write(256, 80, 4096, true, false, cus);
+  CHECK(p.kernel == kKernelStream && p.splits == 3 && p.nb == 3 && p.grid == 240 &&
+        p.compacts && !p.adaptive);
+  // decode_commit_kv1 / kv2: 10 / 20 tiles: 4 token splits x 6 / 3 K parts
+  p = plan_write(256, 10, 4096, true, false, cus);
+  CHECK(p.kernel == kKernelStreamKSplit && p.splits == 4 && p.nb == 2 && p.ksplits == 6 &&
+        p.grid == 256 && p.reduce_grid == 80 && !p.adaptive);
+  p = plan_write(256, 20, 4096, true, false, cus);
+  CHECK(p.kernel == kKernelStreamKSplit && p.splits == 4 && p.ksplits == 3 && !p.adaptive);
+  // wide_gqa_d64: 40 tiles, 512-row window: adaptive, 3 token splits of 128
+  // slots x 2 K parts, one round
+  p = plan_write(512, 40, 7168, true, false, cus);
+  CHECK(p.kernel == kKernelStreamKSplit && p.adaptive && p.splits == 3 && p.nb == 4 &&
+        p.ksplits == 2 && p.grid == 240 && p.reduce_grid == 480);
+  // the same window without commit_lens (every row written): K whole
+  p = plan_write(512, 40, 7168, false, false, cus);
+  CHECK(p.kernel == kKernelStream && !p.adaptive);
+  // prefill_8k: 80 tiles, 8192 rows: tiled, 256-token tiles, five rounds
+  p = plan_write(8192, 80, 4096, false, false, cus);
+  CHECK(p.kernel == kKernelTiled && p.bt == 256 && p.grid == 1280);
+  // biased_fp16: 40 tiles, 2048 rows: 192-token tiles, one round
+  p = plan_write(2048, 40, 3584, false, false, cus);
+  CHECK(p.kernel == kKernelTiled && p.bt == 192 && p.grid == 220);
+  // tiny: 4 tiles, 16 rows
+  p = plan_write(16, 4, 256, false, false, cus);
+  CHECK(p.kernel == kKernelStream && p.splits == 1 && p.nb == 1 && p.grid == 4);
+}
+
 int main() {
   check_eligibility_rules();
   check_window_and_pools();
   check_plans();
+  check_named_plans();
   check_row_validation();
   if (failures) {
     std::fprintf(stderr, "%d checks failed\n", failures);
