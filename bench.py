@@ -134,11 +134,17 @@ def is_attn(workload: str) -> bool:
 
 
 def kernel_source_hash(workload: str = "") -> str:
+    """Hash of the kernel source the workload's counters were taken on, and of
+    the flags it is built with (a change to either makes them stale)."""
     src = (QK_KERNEL_SOURCE if is_qk(workload) else
            VERIFY_KERNEL_SOURCE if is_verify(workload) else
            ATTN_KERNEL_SOURCE if is_attn(workload) else KERNEL_SOURCE)
+    from speculative_decoding_draft_stacked_amd import build as B
+    h = hashlib.sha256()
     with open(src, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+        h.update(f.read())
+    h.update(" ".join(B.SOURCE_FLAGS.get(os.path.basename(src), [])).encode())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):

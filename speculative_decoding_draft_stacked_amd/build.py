@@ -33,6 +33,8 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"),
     "-Wall",
 ]
+# per-source flags (none at present)
+SOURCE_FLAGS: dict = {}
 
 
 def _compile(src: str) -> str:
@@ -40,7 +42,8 @@ def _compile(src: str) -> str:
     if src in HOST_SOURCES:
         cmd = [CXX, *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     else:
-        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o",
+               obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
