@@ -104,6 +104,12 @@ SMALL = {
     # the largest hidden size of the K-split norm (a row of 8192 in registers,
     # 4 waves x 4 passes of 512): 64 tiles x 1 token tile x 4 K parts
     "split_max_h8192": dict(T=64, H=8192, n_aux=1),
+    # 32 tiles x 2 token tiles (the second of 72 tokens) x 4 K parts of 16
+    # chunks
+    "split_t200_h4096": dict(T=200, H=4096, n_aux=1),
+    # fp16 with an fp32 norm weight, a second token tile of 2 tokens, 4 K parts
+    # of 32 chunks
+    "split_fp16_t130": dict(T=130, H=4096, n_aux=2, dtype="fp16", g_fp32=True),
     # K split, fp16 with an fp32 norm weight: 4 tiles x 1 token tile x 4 parts
     "split_fp16": dict(T=128, H=512, n_aux=4, dtype="fp16", g_fp32=True),
 }
