@@ -459,11 +459,17 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
   // from the LDS while the MFMAs of the previous step run, so no MFMA waits
   // on a fragment read issued right before it. Per sub-chunk u:
   //   read step-1 fragments of u | 8 MFMAs on the step-0 fragments of u
-  //   wait for the loads of u + 1, barrier, issue the next loads
+  //   issue the loads of weight sub-chunk u + 3 (into the stage of u - 1)
+  //     and, for even u, of X chunk u / 2 + 1 (into that of chunk u / 2 - 1)
+  //   wait for the loads of u + 1, barrier
   //   read step-0 fragments of u + 1 | 8 MFMAs on the step-1 fragments of u
-  // Whole turns of four sub-chunks (two X chunks) with no branches
-  // (sub-chunks past the end read the zero page), so stage indices are
-  // compile-time constants and every wait count is exact.
+  // The loads go out behind the wave's MFMAs, so a wave held up issuing them
+  // holds up none of its own MFMAs (with the loads placed between the
+  // fragment reads and the MFMAs, prefill took 715 us instead of 588 us;
+  // right after the barrier, 588 us; here, 584 us). Whole turns of four
+  // sub-chunks (two X chunks) with no branches (sub-chunks past the end read
+  // the zero page), so stage indices are compile-time constants and every
+  // wait count is exact.
   auto read_a = [&](int stage, int sp, vec8(&fa)[MB]) {
     const uint16_t* ws = smem + stage * SW;
 #pragma unroll
@@ -509,8 +515,6 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
   for (int u = 0; u < WLOOK; ++u) issue_w(u);
   wait_ring<2 * W_PER_THREAD>();  // X chunk 0 and weight sub-chunk 0
   raw_barrier();
-  issue_x(1);
-  issue_w(WLOOK);
   read_a(0, 0, a0);
   read_b(0, 0, b0);
   for (int c0 = 0; c0 < nsub_ring; c0 += WSTAGES) {
@@ -522,6 +526,11 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
       read_b(uu, 1, b1);
       mfmas(a0, b0);
       __builtin_amdgcn_sched_barrier(0);
+      // the stages of sub-chunk u - 1 (X: chunk u / 2 - 1) were freed by the
+      // previous barrier
+      if (uu % 2 == 0) issue_x((u >> 1) + 1);
+      issue_w(u + WLOOK);
+      __builtin_amdgcn_sched_barrier(0);
       // the loads of sub-chunk u + 1 landed (odd: its X chunk, behind at
       // most two weight sub-chunks; even: its weight sub-chunk, behind one X
       // chunk and two weight sub-chunks), this wave's reads of u are done
@@ -530,8 +539,6 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
       else
         wait_ring<2 * W_PER_THREAD + X_PER_THREAD>();
       raw_barrier();  // ... everyone's: the stages of sub-chunk u are free
-      if ((uu + 1) % 2 == 0) issue_x(((u + 1) >> 1) + 1);
-      issue_w(u + 1 + WLOOK);
       read_a((uu + 1) % WSTAGES, 0, a0);
       read_b(u + 1, 0, b0);
       mfmas(a1, b1);
