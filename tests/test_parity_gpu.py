@@ -532,17 +532,22 @@ def test_rope_tables_by_content():
     assert dk.FALLBACK_REASONS[dk.last_fallback_reason] == "ROPE"
 
 
-@pytest.mark.parametrize("H", [192, 1024], ids=["plain", "k_split"])
-def test_graph_replays_match_eager(H):
+@pytest.mark.parametrize("T,H,kernel", [(96, 192, "stream"), (96, 1024, "stream_ksplit"),
+                                         (4200, 256, "tiled")],
+                         ids=["plain", "k_split", "tiled"])
+def test_graph_replays_match_eager(T, H, kernel):
     """The write captured in a HIP graph (as the benchmark times it) gives the
     eager result on every replay, with eager work and syncs between replays.
     At H = 1024 K is split over workgroups: two launches per write, sharing
-    one caller workspace across replays."""
-    case = W.make_case(T=96, H=H, L=2, NH=2, D=128, row_width=8, slots=256, seed=31)
+    one caller workspace across replays. At 4200 rows (on 256 compute units)
+    the LDS-tiled kernel runs."""
+    case = W.make_case(T=T, H=H, L=2, NH=2, D=128, row_width=8, slots=8192, seed=31)
     dc, pack, _ = _run(case, "eager reference")
     k_ref, v_ref = dc.pools_host()
     ws = dc.workspace(pack)
     assert (ws is not None) == (H == 1024)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert pack.plan(T, True)["kernel"] == kernel
     side = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     dc.reset_pools()
