@@ -199,7 +199,7 @@ def _draw_attn(i):
                 dtype="fp16" if rng.random() < 0.3 else "bf16", seed=9500 + i)
 
 
-@pytest.mark.parametrize("i", range(16))
+@pytest.mark.parametrize("i", range(32))
 def test_random_shapes(i):
     """Seeded sweep: request count, block length (1..48 own keys), grouping
     (1..8 query heads per KV head, so 1..12 row tiles), head_dim, prefix

@@ -162,3 +162,33 @@ def test_graph_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(d.host(), ref), rep
+
+
+# ------------------------------------------------------ seeded shape sweep
+
+N_SWEEP = 24
+
+
+def _draw(i):
+    """Token count, hidden size (a multiple of 128: the 128-feature norm
+    groups), auxiliary layer count, dtype and norm-weight dtype from one seed,
+    across the streaming, K-split and tiled plans; the oracle's work stays
+    under ~2e9 multiply-adds."""
+    rng = np.random.default_rng(7600 + i)
+    H = int(rng.integers(1, 25)) * 128
+    n_aux = int(rng.integers(1, 5))
+    T = int(rng.integers(1, 400)) if rng.random() < 0.6 else int(rng.integers(400, 6000))
+    while T > 1 and T * H * H * n_aux > 2e9:
+        T = T * 2 // 3
+    return dict(name=f"proj_sweep{i}", T=T, H=H, n_aux=n_aux,
+                dtype="fp16" if rng.random() < 0.4 else "bf16", g_fp32=bool(rng.random() < 0.3),
+                eps=float(rng.choice([1e-6, 1e-5])), seed=7600 + i)
+
+
+@pytest.mark.parametrize("i", range(N_SWEEP))
+def test_random_shape(i):
+    kw = _draw(i)
+    c = W.make_proj_case(**kw)
+    d, _, _ = _run(c, kw["name"])
+    say(f"  workspace {d.pack.workspace_bytes(c.T)} bytes")
+

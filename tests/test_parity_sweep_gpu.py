@@ -28,7 +28,7 @@ from gpu_util import DeviceCase, check_slot_sets, compare_rows, say
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 40
+N_CASES = 120
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -81,7 +81,7 @@ def test_random_shape(i):
 
 # ------------------------------------------------ shapes for the K-split form
 
-N_KSPLIT_CASES = 24
+N_KSPLIT_CASES = 64
 
 
 def _draw_ksplit(i):
@@ -128,7 +128,7 @@ def test_random_shape_k_split(i):
 
 # ------------------------------------ shapes for the adaptive K-split plan
 
-N_ADAPTIVE_CASES = 10
+N_ADAPTIVE_CASES = 30
 # (layers, KV heads, head_dim) giving 20, 32, 40, 64 and 80 weight tiles of
 # 128 rows, i.e. 6, 4, 3, 2 and 1 token splits of 128 slots for two K parts
 # on 256 compute units, with the window sizes each plan covers
@@ -179,7 +179,7 @@ def test_random_shape_adaptive(i):
 
 # ------------------------------------------------ shapes for the tiled kernel
 
-N_TILED_CASES = 10
+N_TILED_CASES = 30
 
 
 def _draw_tiled(i):

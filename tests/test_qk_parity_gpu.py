@@ -8,6 +8,7 @@ row (value heads, padding) and every row whose position is outside the table
 must keep its bits exactly.
 """
 
+import dataclasses
 import zlib
 
 import numpy as np
@@ -174,3 +175,41 @@ def test_graph_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(d.host(), ref), rep
+
+
+# ------------------------------------------------------ seeded shape sweep
+
+N_SWEEP = 24
+
+
+def _draw(i):
+    """Head counts, head width, dtype, norm-weight dtype, row padding, table
+    size and base, position pattern (uniform, consecutive, some outside the
+    table) and token count from one seed; sizes keep the oracle to a fraction
+    of a second."""
+    rng = np.random.default_rng(7300 + i)
+    D = int(rng.choice([64, 128]))
+    return dict(name=f"qk_sweep{i}", T=int(rng.integers(1, 1500)), NHQ=int(rng.integers(1, 17)),
+                NHK=int(rng.integers(1, 5)), D=D,
+                dtype="fp16" if rng.random() < 0.4 else "bf16",
+                row_pad=int(rng.choice([0, 0, 8, 40])), weight_fp32=bool(rng.random() < 0.3),
+                theta=float(rng.choice([1e4, 5e4, 1e6])), P=int(rng.choice([64, 4096, 32768])),
+                eps=float(rng.choice([1e-6, 1e-5])), seed=7300 + i,
+                positions_mode=str(rng.choice(["uniform", "arange", "some_out"])))
+
+
+@pytest.mark.parametrize("i", range(N_SWEEP))
+def test_random_shape(i):
+    kw = _draw(i)
+    mode = kw.pop("positions_mode")
+    if mode == "arange":
+        kw["P"] = max(kw["P"], kw["T"])  # consecutive positions stay inside the table
+    c = W.make_qk_case(positions_mode="uniform" if mode == "some_out" else mode, **kw)
+    if mode == "some_out":  # a tenth of the tokens outside the table: untouched, counted
+        rng = np.random.default_rng(7300 + i)
+        pos = c.positions.copy()
+        out = rng.random(c.T) < 0.1
+        pos[out] = rng.choice(np.array([-1, c.P, 1 << 40], dtype=np.int64), int(out.sum()))
+        c = dataclasses.replace(c, positions=pos)
+    _run(c, kw["name"])
+
