@@ -234,3 +234,26 @@ def test_chain_in_one_graph():
                 assert np.array_equal(a, b), rep
             else:
                 assert a == b, rep
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_random_chain(i):
+    """Seeded sweep of whole chains: request count, block length, prefixes,
+    hidden size, layer count, KV heads, grouping, head_dim and dtype drawn per
+    case (sm_scale 1 so that outputs follow their best keys)."""
+    rng = np.random.default_rng(8100 + i)
+    B = int(rng.integers(1, 6))
+    D = int(rng.choice([64, 128]))
+    NH = int(rng.choice([1, 2, 4]))
+    kw = dict(B=B, block=int(rng.integers(1, 17)),
+              prefix=[int(x) for x in rng.integers(1, 600, size=B)],
+              H=int(rng.integers(2, 9)) * 128, L=int(rng.integers(1, 4)), NH=NH,
+              NHQ=NH * int(rng.choice([1, 2, 4])), D=D,
+              dtype="fp16" if rng.random() < 0.4 else "bf16", sm_scale=1.0)
+    s = W.make_draft_step(name=f"chain{i}", seed=8100 + i, **kw)
+    say(f"[chain {i}] {kw}")
+    dev = DeviceStep(s)
+    dev.reset()
+    dev.run()
+    _check(s, dev.results(), oracle_chain(s))
+

@@ -113,3 +113,23 @@ def test_graph_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(acc, acc_ref) and torch.equal(bon, bon_ref), rep
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_shapes(i):
+    """Seeded sweep: request count 1..3000, draft length 0..260, vocabulary 2
+    to 2^40 (64-bit ids), matched-prefix lengths from the generator, row
+    padding; compared exactly."""
+    rng = np.random.default_rng(7900 + i)
+    B = int(rng.integers(1, 3001))
+    K = int(rng.choice([int(rng.integers(0, 9)), int(rng.integers(9, 66)),
+                        int(rng.integers(66, 261))]))
+    vocab = int(rng.choice([2, 7, 151936, 1 << 40]))
+    if K == 0:
+        draft = np.zeros((B, 0), dtype=np.int64)
+        target = rng.integers(0, vocab, size=(B, 1), dtype=np.int64)
+    else:
+        c = W.make_verify_case(B=B, K=K, vocab=vocab, seed=7900 + i)
+        draft, target = c.draft, c.target
+    _run(draft, target, f"verify_sweep{i}", pad=int(rng.choice([0, 3])))
+
