@@ -400,29 +400,13 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
   const int64_t n0 = rp * ROWS;
   const int64_t t0 = tt * BT;
 
-  // Per-lane sources for the first half of chunk 0. Stage piece q of the
-  // weight is (block q / 512, group g, step s' of the half, lane l).
-  const uint16_t* wsrc[W_PER_THREAD];
-#pragma unroll
-  for (int i = 0; i < W_PER_THREAD; ++i) {
-    const int q = i * NT + tid;
-    const int64_t rt = 2 * rp + q / 512;
-    const int g = (q % 512) / 128, sp = (q % 128) / 64, l = q % 64;
-    wsrc[i] = rt < R ? a.w + rt * nk * 8192 + ((g * 4 + sp) * 64 + l) * 8 : nullptr;
-  }
-  // X slot (i * NT + tid) of a chunk: token slot / 8, LDS piece slot % 8,
-  // holding global piece (slot % 8) ^ ((t / 2) % 8) of the token's 64 columns
-  int64_t xoff[X_PER_THREAD];
-  int xcol[X_PER_THREAD];
-#pragma unroll
-  for (int i = 0; i < X_PER_THREAD; ++i) {
-    const int slot = i * NT + tid;
-    const int t = slot / 8;
-    const int col = 8 * ((slot % 8) ^ ((t >> 1) & 7));
-    const int64_t tok = t0 + t < T ? t0 + t : T - 1;  // rows past T are never stored
-    xoff[i] = tok * a.x_stride + col;
-    xcol[i] = col;
-  }
+  // Per-lane source offsets: weight stage piece q = i * NT + tid is (block i,
+  // group tid / 128, step (tid / 64) % 2, lane tid % 64); X slot i * NT + tid
+  // is token i * 64 + tid / 8, LDS piece tid % 8 holding global piece
+  // (tid % 8) ^ ((tid / 16) % 8) (the same column offset for every i).
+  const int wl = ((tid / 128) * 4 + (tid % 128) / 64) * 512 + (tid % 64) * 8;
+  const int xt = tid / 8;
+  const int xcol = 8 * ((tid & 7) ^ ((xt >> 1) & 7));
   // weight sub-chunk u (half u % 2 of 64-column chunk u / 2) into stage u % 4;
   // the second half takes MFMA steps 2 and 3
   auto issue_w = [&](int u) {
@@ -431,18 +415,22 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
     const bool live = c < nk;  // sub-chunks past the end read the zero page
 #pragma unroll
     for (int i = 0; i < W_PER_THREAD; ++i) {
-      const uint16_t* src = live && wsrc[i] ? wsrc[i] + (int64_t)c * 8192 + h * 1024 : a.zeros;
+      const int64_t rt = 2 * rp + i;
+      const uint16_t* src =
+          live && rt < R ? a.w + (rt * nk + c) * 8192 + h * 1024 + wl : a.zeros;
       ldg16_to_lds(src, base + (i * NT + wave * 64) * 8);
     }
   };
   // X chunk c (64 columns of every token of the tile) into stage c % 2
   auto issue_x = [&](int c) {
     uint16_t* base = smem + XOFF + (c & 1) * SX;
-    const bool live = c < nk;
+    const int k = c * BK + xcol;
+    const bool live = c < nk && k < H;
 #pragma unroll
     for (int i = 0; i < X_PER_THREAD; ++i) {
-      const int k = c * BK + xcol[i];
-      const uint16_t* src = live && k < H ? a.x + xoff[i] + c * BK : a.zeros;
+      const int64_t t = t0 + i * 64 + xt;
+      const int64_t tok = t < T ? t : T - 1;  // rows past T are never stored
+      const uint16_t* src = live ? a.x + tok * a.x_stride + k : a.zeros;
       ldg16_to_lds(src, base + (i * NT + wave * 64) * 8);
     }
   };
@@ -466,7 +454,12 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
   // The loads go out behind the wave's MFMAs, so a wave held up issuing them
   // holds up none of its own MFMAs (with the loads placed between the
   // fragment reads and the MFMAs, prefill took 715 us instead of 588 us;
-  // right after the barrier, 588 us; here, 584 us). Whole turns of four
+  // right after the barrier, 588 us; here, 584 us). A step's fragment reads
+  // are interleaved one per MFMA with the previous step's MFMAs, and the
+  // load addresses are formed from the tile's scalars at each issue rather
+  // than kept in per-lane arrays (230-238 VGPRs instead of 248: 573 against
+  // 580 us on prefill; placing all six reads ahead of the MFMAs instead
+  // needs 256 VGPRs and took 608 us). Whole turns of four
   // sub-chunks (two X chunks) with no branches (sub-chunks past the end read
   // the zero page), so stage indices are compile-time constants and every
   // wait count is exact.
@@ -525,6 +518,12 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
       read_a(uu, 1, a1);
       read_b(uu, 1, b1);
       mfmas(a0, b0);
+#pragma unroll
+      for (int g = 0; g < MB + NB; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, MB * NB - (MB + NB), 0);
       __builtin_amdgcn_sched_barrier(0);
       // the stages of sub-chunk u - 1 (X: chunk u / 2 - 1) were freed by the
       // previous barrier
@@ -542,6 +541,12 @@ __global__ __launch_bounds__(512) void ctx_kv_tiled_kernel(const WriteArgs a, in
       read_a((uu + 1) % WSTAGES, 0, a0);
       read_b(u + 1, 0, b0);
       mfmas(a1, b1);
+#pragma unroll
+      for (int g = 0; g < MB + NB; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, MB * NB - (MB + NB), 0);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
